@@ -1,0 +1,214 @@
+"""CPU float64 oracle of the gpt-oss MoE block forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The
+product path (the HIP library and its Python binding) never imports it, and
+this module imports nothing from the product path: its only inputs are numpy
+arrays of bfloat16 bit patterns.
+
+What it computes, and where the pages define it (xserv "Phase 19: gpt-oss-20b
+MoE support" page):
+
+* section 1, architecture table, row "MoE": a plain Linear router with bias
+  over the hidden state, 32 experts, top-4, expert intermediate size 2880;
+* section 1, architecture table, row for the activation: the clamped,
+  interleaved GLU -- gate is the even columns of the gate_up output, up the odd
+  ones, gate is clamped from above at 7, up to [-7, 7], and
+  h = (up + 1) * gate * sigmoid(1.702 * gate);
+* section 2, the forward pipeline: router -> top-k softmax -> gate_up GEMM ->
+  bias -> GLU -> down GEMM -> bias -> weighted sum over the top-4 experts only,
+  with unselected experts skipped rather than multiplied by zero.
+
+Everything is computed in float64 from the exactly widened bf16 inputs;
+nothing is rounded except where a reading below says so.
+
+Readings where the pages are silent (each is listed in the design doc):
+
+* R1  softmax over the k selected logits (softmax over all E followed by
+      renormalising over the top k is the same number);
+* R2  top-k order is (logit descending, expert index ascending); equal logits
+      go to the lower index;
+* R3  the top-k *decision* is taken on the logits rounded to float32, the
+      precision the GPU kernel decides in; weights use the float64 logits;
+* R4  biases are added before the clamp (gate_up) and inside the weighted sum
+      (down), i.e. y = sum_j w_j * (h_j @ Wd[e_j] + bd[e_j]);
+* R5  the clamped gate value is used in both factors of gate*sigmoid(1.702*gate);
+      up is clamped first, then 1 is added.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GLU_ALPHA = 1.702     # sigmoid slope of the GLU (architecture table, activation row)
+GLU_LIMIT = 7.0       # clamp bound of gate (upper) and up (both sides)
+
+
+# --------------------------------------------------------------------------
+# bf16 bit patterns -> float64 (exact widening: every bf16 is a float32)
+# --------------------------------------------------------------------------
+def widen(bits: np.ndarray) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Router (section 1 "MoE" row: Linear[H -> E] + bias; section 2 step 1)
+# --------------------------------------------------------------------------
+def router_logits(x, Wr, br) -> np.ndarray:
+    """logits[t, e] = sum_h x[t, h] * Wr[e, h] + br[e], float64, shape [T, E]."""
+    return widen(x) @ widen(Wr).T + widen(br)[None, :]
+
+
+def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
+    """Top-k expert ids per row, ordered by (value desc, index asc).  [T, k] int32.
+
+    The comparison uses the values as given (the caller passes the float32
+    logits, reading R3).  -0.0 and +0.0 compare equal, so they tie and the
+    lower index wins."""
+    T, E = logits.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    idx = np.arange(E)
+    for t in range(T):
+        v = logits[t]
+        # lexsort sorts by the last key first: primary key -value, then index
+        order = np.lexsort((idx, -v.astype(np.float64)))
+        ids[t] = order[:k]
+    return ids
+
+
+def routing_weights(logits64: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """Softmax over the k selected logits (reading R1).  [T, k] float64."""
+    sel = np.take_along_axis(logits64, ids.astype(np.int64), axis=1)
+    m = sel.max(axis=1, keepdims=True)
+    ex = np.exp(sel - m)
+    return ex / ex.sum(axis=1, keepdims=True)
+
+
+def route(x, Wr, br, k: int):
+    """moe_route: returns (ids [T,k] int32, w [T,k] float64, logits float64)."""
+    lg = router_logits(x, Wr, br)
+    ids = select_topk(lg.astype(np.float32), k)
+    w = routing_weights(lg, ids)
+    return ids, w, lg
+
+
+# --------------------------------------------------------------------------
+# Expert MLP (section 1 activation row; section 2 gate_up -> bias -> GLU ->
+# down -> bias)
+# --------------------------------------------------------------------------
+def clamped_glu(u: np.ndarray) -> np.ndarray:
+    """h[..., i] from the interleaved gate_up pre-activation u[..., 2I]."""
+    gate = np.minimum(u[..., 0::2], GLU_LIMIT)
+    up = np.clip(u[..., 1::2], -GLU_LIMIT, GLU_LIMIT)
+    glu = gate / (1.0 + np.exp(-GLU_ALPHA * gate))
+    return (up + 1.0) * glu
+
+
+def expert_mlp(xrows64: np.ndarray, Wgu_e64, bgu_e64, Wd_e64, bd_e64):
+    """One expert applied to rows of x: returns (u, h, o), all float64."""
+    u = xrows64 @ Wgu_e64 + bgu_e64
+    h = clamped_glu(u)
+    o = h @ Wd_e64 + bd_e64
+    return u, h, o
+
+
+# --------------------------------------------------------------------------
+# Expert-contiguous permutation (the device-side bookkeeping that replaces
+# copying every token to every expert, section 2)
+# --------------------------------------------------------------------------
+def expert_permutation(ids: np.ndarray, E: int):
+    """Counting sort of the T*k (token, slot) pairs by expert, stable in slot order.
+
+    Returns cnt [E], off [E+1] (exclusive prefix sum), rows [T*k] (rows[off[e]+r]
+    is the r-th slot s = t*k + j routed to e, in increasing s) and pos [T*k]
+    (the inverse: rows[pos[s]] == s)."""
+    flat = ids.reshape(-1).astype(np.int64)
+    cnt = np.zeros(E, dtype=np.int64)
+    for e in flat:
+        cnt[e] += 1
+    off = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        off[e + 1] = off[e] + cnt[e]
+    fill = off[:-1].copy()
+    rows = np.empty(flat.size, dtype=np.int64)
+    pos = np.empty(flat.size, dtype=np.int64)
+    for s, e in enumerate(flat):
+        rows[fill[e]] = s
+        pos[s] = fill[e]
+        fill[e] += 1
+    return (cnt.astype(np.int32), off.astype(np.int32), rows.astype(np.int32),
+            pos.astype(np.int32))
+
+
+# --------------------------------------------------------------------------
+# Whole block, sparse formulation: only selected experts are read
+# --------------------------------------------------------------------------
+def moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k: int, tokens=None, keep=False):
+    """Full forward.  Returns a dict with y [T', H] float64, ids, w, logits,
+    and, if keep, u/h/o per slot [T'*k, ...] in slot order s = t*k + j.
+
+    tokens: optional array of token indices; the result then covers only those
+    rows of x (used to check sampled outputs at full size)."""
+    ids, w, lg = route(x if tokens is None else x[np.asarray(tokens)], Wr, br, k)
+    xs = widen(x if tokens is None else x[np.asarray(tokens)])
+    T, H = xs.shape
+    E = Wr.shape[0]
+    y = np.zeros((T, Wd.shape[2]), dtype=np.float64)
+    I2 = Wgu.shape[2]
+    if keep:
+        u_all = np.zeros((T * k, I2))
+        h_all = np.zeros((T * k, I2 // 2))
+        o_all = np.zeros((T * k, Wd.shape[2]))
+    flat = ids.reshape(-1)
+    for e in range(E):
+        slots = np.nonzero(flat == e)[0]
+        if slots.size == 0:
+            continue               # skipped, never multiplied by zero
+        toks = slots // k
+        u, h, o = expert_mlp(xs[toks], widen(Wgu[e]), widen(bgu[e]), widen(Wd[e]), widen(bd[e]))
+        ws = w.reshape(-1)[slots]
+        np.add.at(y, toks, ws[:, None] * o)
+        if keep:
+            u_all[slots], h_all[slots], o_all[slots] = u, h, o
+    out = {"y": y, "ids": ids, "w": w, "logits": lg}
+    if keep:
+        out.update(u=u_all, h=h_all, o=o_all)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Second formulation: every expert on every token, then select (the dense
+# "replicate to all local experts" pipeline of section 2).  Small shapes only.
+# --------------------------------------------------------------------------
+def moe_forward_dense(x, Wr, br, Wgu, bgu, Wd, bd, k: int):
+    ids, w, lg = route(x, Wr, br, k)
+    xs = widen(x)
+    E = Wr.shape[0]
+    outs = np.stack([expert_mlp(xs, widen(Wgu[e]), widen(bgu[e]), widen(Wd[e]), widen(bd[e]))[2]
+                     for e in range(E)])          # [E, T, H]
+    T = xs.shape[0]
+    y = np.zeros((T, Wd.shape[2]))
+    for t in range(T):
+        for j in range(k):
+            y[t] += w[t, j] * outs[ids[t, j], t]
+    return {"y": y, "ids": ids, "w": w, "logits": lg}
+
+
+# --------------------------------------------------------------------------
+# Diagnostics reported next to the comparisons
+# --------------------------------------------------------------------------
+def near_ties(logits64: np.ndarray, k: int, rel: float = 1e-5) -> np.ndarray:
+    """Tokens whose float64 gap at any rank boundary 1|2 ... k|k+1 is below
+    rel * max(1, |logit|): the tokens where a float32 router could differ."""
+    s = -np.sort(-logits64, axis=1)
+    kk = min(k + 1, s.shape[1])
+    gaps = s[:, :kk - 1] - s[:, 1:kk]
+    scale = np.maximum(1.0, np.abs(s[:, :kk - 1]))
+    return np.nonzero((gaps < rel * scale).any(axis=1))[0]
+
+
+def clamp_fraction(u: np.ndarray) -> float:
+    """Fraction of gate/up pre-activations that the GLU clamps (gate > 7 or |up| > 7)."""
+    g = u[..., 0::2]
+    p = u[..., 1::2]
+    return float(((g > GLU_LIMIT).sum() + (np.abs(p) > GLU_LIMIT).sum()) / u.size)
