@@ -1,0 +1,225 @@
+"""Benchmark of the MI355X MoE block forward (one JSON line on stdout).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
+
+A step is one whole moe_forward (router + top-k + permutation + gate_up/GLU +
+down + combine) over one batch of seeded synthetic input already resident in
+HBM.  The default workload is the gpt-oss-20b MoE block at decode batch
+T = 64 (H = I = 2880, E = 32, top-4, bf16 weights N(0, 0.02), biases N(0, 0.01),
+router bias 0, x scaled so ~5% of gate/up pre-activations hit the clamp,
+seed 0).  `value` is tokens per second of the whole job.
+
+Two extra objects:
+  roofline      the dominant kernel (the gate_up expert kernel, two thirds of
+                the bytes): algorithmic bytes per launch / its mean launch time,
+                timed with HIP events on the stream it runs on;
+  cpu_baseline  the float64 oracle timed on the host cores over a bounded
+                sample of the same workload (a baseline, not the target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE-layer tokens/sec + % of HBM or bf16 MFMA roofline on 1 MI355X"
+
+
+def _alg_bytes_layer(cfg, D):
+    """Bytes the method must move: weights and biases of the D live experts,
+    the router, x read once and y written once."""
+    H, I, E, T = cfg.H, cfg.I, cfg.E, cfg.T
+    per_expert = H * 2 * I * 2 + I * H * 2 + 2 * I * 2 + H * 2
+    return D * per_expert + E * H * 2 + E * 2 + 2 * T * H * 2
+
+
+def _alg_bytes_gate_up(cfg, D):
+    """gate_up launch: live experts' Wgu and bgu, x read once, h written once."""
+    H, I, T, k = cfg.H, cfg.I, cfg.T, cfg.k
+    return D * (H * 2 * I * 2 + 2 * I * 2) + T * H * 2 + T * k * I * 2
+
+
+def _alg_flops_layer(cfg):
+    H, I, E, T, k = cfg.H, cfg.I, cfg.E, cfg.T, cfg.k
+    return T * (2 * H * E + k * (2 * H * 2 * I + 2 * I * H))
+
+
+def _source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_file, workload, launches_bytes_unit=1.0):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel_file.split('/')[-1].split('.')[0]}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("source_digest") != _source_digest([kernel_file, "moe_layer_route_amd/csrc/device_common.h"]):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, k, min_seconds=10.0, max_reps=3):
+    """The float64 oracle on the host cores over the whole workload, repeated
+    until about min_seconds of CPU time (at most max_reps runs)."""
+    import numpy as np
+    import oracle.moe_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < max_reps and (time.perf_counter() - t_all) < min_seconds:
+        t0 = time.perf_counter()
+        orc.moe_forward(*inp.arrays(), k=k)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": inp.cfg.T / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"whole {inp.cfg.name} batch (T={inp.cfg.T}) through the float64 numpy oracle, "
+                      f"median of {len(times)} runs of {t:.2f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from moe_layer_route_amd import binding, datagen as d
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = d.CONFIGS[args.workload]
+    inp = d.make_inputs(cfg, seed=0)
+    print(f"[bench] inputs ready: {cfg.name} T={cfg.T} E={cfg.E}", file=sys.stderr, flush=True)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    x, Wr, br, Wgu, bgu, Wd, bd = [dev(a) for a in inp.arrays()]
+    T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+    ws = binding.alloc_workspace(T, H, E, k, I)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        binding.moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k=k, y=y, workspace=ws, topk_ids=ids, topk_w=w,
+                            path=args.path, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # Dominant kernel: the same pipeline through the stage calls, with events
+    # around every gate_up launch on the stream it is launched on.
+    cnt, off, rows, pos = binding.moe_permute(ids, E, stream=stream)
+    h = torch.empty((T * k, I), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def stage_step(ev=None):
+        binding.moe_route(x, Wr, br, k, topk_ids=ids, topk_w=w, stream=stream)
+        binding.library().moe_permute(binding._ptr(ids), T, E, k, binding._ptr(cnt), binding._ptr(off),
+                                      binding._ptr(rows), binding._ptr(pos), binding._stream(stream))
+        if ev:
+            ev[0].record(stream)
+        binding.moe_gate_up(x, Wgu, bgu, cnt, off, rows, k, path=args.path, h=h, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        binding.moe_down(h, Wd, bd, cnt, off, T, k, path=args.path, o=o, stream=stream)
+        binding.moe_combine(o, pos, w, y=y, stream=stream)
+
+    for _ in range(max(2, args.warmup // 2)):
+        stage_step()
+    torch.cuda.synchronize()
+    for ev in evs:
+        stage_step(ev)
+    torch.cuda.synchronize()
+    gate_up_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    D = int((torch.bincount(ids.reshape(-1).long(), minlength=E) > 0).sum().item())
+    gu_bytes = _alg_bytes_gate_up(cfg, D)
+    achieved = gu_bytes / (gate_up_ms * 1e-3) / 1e9
+    gu_file = "moe_layer_route_amd/csrc/gemv.hip"
+    traffic = _traffic(gu_file, cfg.name)
+    layer_bytes = _alg_bytes_layer(cfg, D)
+    layer_flops = _alg_flops_layer(cfg)
+    step_s = ms_per_step * 1e-3
+
+    out = {
+        "metric": METRIC,
+        "value": T / step_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal bf16 inputs of the gpt-oss MoE block shapes; random-init weights)",
+        "config": {"workload": f"{cfg.name}: {cfg.description}", "T": T, "H": H, "I": I, "E": E, "k": k,
+                   "seed": 0, "path": args.path, "live_experts": D},
+        "roofline": {"bound": "hbm", "kernel": "gemv_expert_kernel<gate_up>", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "alg_bytes_per_launch": gu_bytes, "launch_us": gate_up_ms * 1e3},
+        "layer": {"alg_bytes": layer_bytes, "alg_flops": layer_flops,
+                  "hbm_GBs": layer_bytes / step_s / 1e9, "hbm_frac": layer_bytes / step_s / 1e9 / HBM_PEAK_GBS,
+                  "tflops": layer_flops / step_s / 1e12,
+                  "mfma_frac": layer_flops / step_s / 1e12 / BF16_PEAK_TFLOPS},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, k)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

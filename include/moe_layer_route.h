@@ -1,0 +1,203 @@
+/*
+ * moe_layer_route.h -- C ABI of the MI355X (gfx950) gpt-oss MoE block forward.
+ *
+ * The operation is the MoE block of gpt-oss as the xserv page "Phase 19:
+ * gpt-oss-20b MoE support" describes it:
+ *   - section 1, architecture table, "MoE" row: a plain Linear router with
+ *     bias, E experts, top-k (gpt-oss: 32 or 128 experts, k = 4), expert
+ *     intermediate size I (2880), hidden size H (2880, not a multiple of 128);
+ *   - section 1, architecture table, activation row: the clamped interleaved
+ *     GLU  gate = gu[0::2], up = gu[1::2], gate <= 7, up in [-7, 7],
+ *     h = (up + 1) * gate * sigmoid(1.702 * gate);
+ *   - section 2, forward pipeline: router -> top-k softmax -> per-expert
+ *     gate_up GEMM -> bias -> GLU -> per-expert down GEMM -> bias -> weighted
+ *     sum over the k selected experts only (unselected experts are skipped,
+ *     never multiplied by 0); the expert ids stay on the device and the host
+ *     never synchronises.
+ *
+ * Conventions for every call below:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees, copies to the host or synchronises the
+ *     host.  Inputs are never modified.
+ *   - bf16 means IEEE bfloat16 (stored as 16-bit words); all tensors are
+ *     row-major and densely packed.
+ *   - Every pointer that is read or written with 16-byte vector accesses
+ *     (x, Wr, Wgu, Wd, h, o, y and the workspace) must be 16-byte aligned;
+ *     bias, id, weight and index arrays must be 4-byte aligned.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns at once.  Results are valid once the
+ *     stream reaches the call.  Nothing depends on host-side state between
+ *     calls, so the calls can be captured in a HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns a non-zero status and enqueues nothing.  A failed
+ *     launch returns MOE_ERR_HIP.  moe_last_error() gives a message for the
+ *     last failing call on the calling thread.  No exception crosses the ABI.
+ *   - T = 0 is a valid call that enqueues nothing.
+ *   - Limits: 1 <= E <= 256, 1 <= k <= min(E, 8), 8 <= H, I <= 16384 with
+ *     H % 8 == 0 and I % 8 == 0, 0 <= T and T * k < 2^31.
+ *   - Results are bitwise reproducible: no floating-point atomics are used.
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef MOE_LAYER_ROUTE_H
+#define MOE_LAYER_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Every entry point is exported from the shared library. */
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_E 256
+#define MOE_MAX_K 8
+#define MOE_MAX_DIM 16384
+
+/* Status codes returned by every call that can fail. */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG 1   /* null/misaligned pointer, bad size or k */
+#define MOE_ERR_UNSUPPORTED 2   /* valid request the library does not implement */
+#define MOE_ERR_WORKSPACE 3     /* workspace missing or smaller than moe_workspace_bytes() */
+#define MOE_ERR_HIP 4           /* a HIP launch or runtime call failed */
+
+/* Execution path of the expert GEMMs (moe_forward_ex, moe_gate_up, moe_down). */
+#define MOE_PATH_AUTO 0   /* chosen on the host from T*k/E only */
+#define MOE_PATH_GEMV 1   /* weight streaming: each weight byte read once per pass of <=32 rows */
+#define MOE_PATH_GEMM 2   /* LDS-tiled MFMA grouped GEMM */
+
+/* Version of this ABI (MOE_ABI_VERSION). */
+MOE_API int moe_abi_version(void);
+
+/* Static text for a status code. */
+MOE_API const char* moe_status_str(int status);
+
+/* Message describing the last failing call made on this thread ("" if none). */
+MOE_API const char* moe_last_error(void);
+
+/*
+ * Bytes of device workspace that moe_forward / moe_forward_ex need for these
+ * sizes (0 when T == 0).  The caller allocates it (any 256-byte aligned
+ * device buffer, contents irrelevant) and may reuse it across calls.
+ * Returns 0 and sets moe_last_error() for sizes outside the limits.
+ */
+MOE_API size_t moe_workspace_bytes(int64_t T, int32_t H, int32_t E, int32_t k, int32_t I);
+
+/*
+ * moe_route -- router logits, top-k and softmax weights
+ * (architecture table "MoE" row; forward pipeline, first two steps).
+ *
+ *   x   bf16 [T][H]     token activations
+ *   Wr  bf16 [E][H]     router weight (Linear form: one row per expert)
+ *   br  bf16 [E]        router bias
+ *   topk_ids  int32 [T][k]  out: the k experts with the largest logits
+ *                           l[t][e] = sum_h x[t][h] * Wr[e][h] + br[e], ordered
+ *                           by (logit descending, expert index ascending); equal
+ *                           logits go to the lower index.  The decision is made
+ *                           on the logits rounded to float32 from a float64
+ *                           accumulation.
+ *   topk_w    float [T][k]  out: softmax over the k selected logits
+ *                           (w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0)); each
+ *                           row sums to 1.
+ */
+MOE_API int moe_route(const void* x, const void* Wr, const void* br,
+              int64_t T, int32_t H, int32_t E, int32_t k,
+              int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
+ * moe_forward -- the whole MoE block forward (forward pipeline, all steps).
+ *
+ *   x, Wr, br       as in moe_route
+ *   Wgu  bf16 [E][H][2I]   gate_up weight in x.W form; output columns are
+ *                          interleaved gate0, up0, gate1, up1, ...
+ *   bgu  bf16 [E][2I]      gate_up bias, interleaved the same way
+ *   Wd   bf16 [E][I][H]    down weight in x.W form
+ *   bd   bf16 [E][H]       down bias
+ *   y    bf16 [T][H]       out: y[t] = sum_j w[t][j] * (h_j . Wd[e_j] + bd[e_j]),
+ *                          h_j = GLU(x[t] . Wgu[e_j] + bgu[e_j]); products in
+ *                          bf16 x bf16, accumulation in float32, h rounded to
+ *                          bf16 before the down GEMM, y rounded once to bf16.
+ *   topk_ids_out, topk_w_out   optional outputs (NULL to skip) of the routing
+ *                          decision, same meaning as in moe_route.
+ *   workspace, workspace_bytes  scratch of at least moe_workspace_bytes(...).
+ */
+MOE_API int moe_forward(const void* x, const void* Wr, const void* br,
+                const void* Wgu, const void* bgu, const void* Wd, const void* bd,
+                int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                void* y, int32_t* topk_ids_out, float* topk_w_out,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_forward with the expert path forced (MOE_PATH_*); used to test both
+ * paths at every shape.  moe_forward is moe_forward_ex(..., MOE_PATH_AUTO). */
+MOE_API int moe_forward_ex(const void* x, const void* Wr, const void* br,
+                   const void* Wgu, const void* bgu, const void* Wd, const void* bd,
+                   int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                   void* y, int32_t* topk_ids_out, float* topk_w_out,
+                   void* workspace, size_t workspace_bytes, int32_t path, void* stream);
+
+/*
+ * moe_permute -- expert-contiguous order of the T*k (token, slot) pairs: the
+ * device-side bookkeeping that replaces copying every token to every expert
+ * (forward pipeline; ids never leave the device).
+ *
+ *   topk_ids int32 [T][k]  in
+ *   cnt  int32 [E]    out: number of slots routed to each expert
+ *   off  int32 [E+1]  out: exclusive prefix sum of cnt (off[E] = T*k)
+ *   rows int32 [T*k]  out: rows[off[e] + r] = the r-th slot s = t*k + j with
+ *                     topk_ids[t][j] == e, in increasing s (stable)
+ *   pos  int32 [T*k]  out: inverse of rows (rows[pos[s]] == s)
+ * Every id must lie in [0, E); other values are undefined behaviour.
+ */
+MOE_API int moe_permute(const int32_t* topk_ids, int64_t T, int32_t E, int32_t k,
+                int32_t* cnt, int32_t* off, int32_t* rows, int32_t* pos, void* stream);
+
+/*
+ * moe_gate_up -- per-expert gate_up GEMM + bias + clamped GLU for all experts
+ * in one launch (architecture table activation row; forward pipeline).
+ *
+ *   x bf16 [T][H], Wgu bf16 [E][H][2I], bgu bf16 [E][2I]
+ *   cnt, off, rows    as produced by moe_permute
+ *   h  bf16 [T*k][I]  out, in permuted order: h[off[e] + r] belongs to slot
+ *                     rows[off[e] + r] (token rows[...] / k) and expert e.
+ *   path              MOE_PATH_* (AUTO picks from T*k/E)
+ */
+MOE_API int moe_gate_up(const void* x, const void* Wgu, const void* bgu,
+                const int32_t* cnt, const int32_t* off, const int32_t* rows,
+                int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                void* h, int32_t path, void* stream);
+
+/*
+ * moe_down -- per-expert down GEMM + bias for all experts in one launch.
+ *
+ *   h  bf16 [T*k][I] in permuted order (moe_gate_up), Wd bf16 [E][I][H],
+ *   bd bf16 [E][H], cnt/off as produced by moe_permute
+ *   o  float [T*k][H] out, permuted order: o[off[e]+r] = h[off[e]+r] . Wd[e] + bd[e]
+ */
+MOE_API int moe_down(const void* h, const void* Wd, const void* bd,
+             const int32_t* cnt, const int32_t* off,
+             int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+             float* o, int32_t path, void* stream);
+
+/*
+ * moe_combine -- routing-weighted sum over each token's k expert outputs,
+ * summed in float32 in the fixed order j = 0..k-1 and rounded once to bf16.
+ * Only the selected slots are read.
+ *
+ *   o float [T*k][H] (moe_down), pos int32 [T*k] (moe_permute),
+ *   topk_w float [T][k] (moe_route)
+ *   y bf16 [T][H] out: y[t] = sum_j topk_w[t][j] * o[pos[t*k + j]]
+ */
+MOE_API int moe_combine(const float* o, const int32_t* pos, const float* topk_w,
+                int64_t T, int32_t H, int32_t k, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LAYER_ROUTE_H */

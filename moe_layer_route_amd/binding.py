@@ -1,0 +1,202 @@
+"""Thin Python binding of the C ABI in ``include/moe_layer_route.h``.
+
+Argument marshalling only: every step of the MoE block runs in the HIP kernels
+of ``libmoe_layer_route.so``.  PyTorch provides device memory (``torch.empty``)
+and the current stream; nothing here computes on tensor values.  If the
+library has not been built, every call raises ``MoEError`` -- there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
+_PATHS = {"auto": PATH_AUTO, "gemv": PATH_GEMV, "gemm": PATH_GEMM}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_layer_route.so")
+
+EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace_bytes", "moe_route",
+           "moe_forward", "moe_forward_ex", "moe_permute", "moe_gate_up", "moe_down", "moe_combine")
+
+
+class MoEError(RuntimeError):
+    """A call into the native library failed (or the library is missing)."""
+
+
+_lib = None
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_SIGS = {
+    "moe_abi_version": (ctypes.c_int, []),
+    "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32]),
+    "moe_route": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "moe_forward": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _vp]),
+    "moe_forward_ex": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _i32, _vp]),
+    "moe_permute": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "moe_gate_up": (ctypes.c_int, [_vp] * 6 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
+    "moe_down": (ctypes.c_int, [_vp] * 5 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
+    "moe_combine": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
+}
+
+
+def library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the native library (once).  Raises MoEError if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise MoEError(f"native library not built: {path} (run __graft_entry__.build())")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        lib = library()
+        msg = lib.moe_last_error().decode()
+        raise MoEError(f"{what}: {lib.moe_status_str(status).decode()} ({status}): {msg}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise MoEError("tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise MoEError("tensors must be contiguous")
+
+
+def _b16(*ts):
+    for t in ts:
+        if t.element_size() != 2:
+            raise MoEError(f"expected a 2-byte (bf16) tensor, got {t.dtype}")
+
+
+def path_code(path) -> int:
+    if isinstance(path, str):
+        return _PATHS[path]
+    return int(path)
+
+
+def workspace_bytes(T: int, H: int, E: int, k: int, I: int) -> int:
+    return int(library().moe_workspace_bytes(T, H, E, k, I))
+
+
+def alloc_workspace(T: int, H: int, E: int, k: int, I: int, device=None) -> torch.Tensor:
+    n = workspace_bytes(T, H, E, k, I)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def moe_route(x, Wr, br, k: int, topk_ids=None, topk_w=None, stream=None):
+    """Router: returns (topk_ids int32 [T,k], topk_w float32 [T,k])."""
+    _dev(x, Wr, br)
+    _b16(x, Wr, br)
+    T, H = x.shape
+    E = Wr.shape[0]
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _dev(topk_ids, topk_w)
+    _check(library().moe_route(_ptr(x), _ptr(Wr), _ptr(br), T, H, E, k, _ptr(topk_ids), _ptr(topk_w),
+                               _stream(stream)), "moe_route")
+    return topk_ids, topk_w
+
+
+def moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k: int = 4, y=None, workspace=None, topk_ids=None,
+                topk_w=None, path="auto", stream=None):
+    """Whole MoE block forward; returns y (bf16 [T,H]).
+
+    topk_ids / topk_w: optional preallocated outputs of the routing decision.
+    workspace: optional uint8 device buffer of at least workspace_bytes(...)."""
+    _dev(x, Wr, br, Wgu, bgu, Wd, bd)
+    _b16(x, Wr, br, Wgu, bgu, Wd, bd)
+    T, H = x.shape
+    E = Wr.shape[0]
+    I = Wd.shape[1]
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(T, H, E, k, I, x.device)
+    _dev(y, workspace, topk_ids, topk_w)
+    st = library().moe_forward_ex(_ptr(x), _ptr(Wr), _ptr(br), _ptr(Wgu), _ptr(bgu), _ptr(Wd), _ptr(bd),
+                                  T, H, E, k, I, _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), path_code(path),
+                                  _stream(stream))
+    _check(st, "moe_forward")
+    return y
+
+
+def moe_forward_ex(*args, **kw):
+    return moe_forward(*args, **kw)
+
+
+def moe_permute(topk_ids, E: int, stream=None):
+    """Expert-contiguous order: returns (cnt [E], off [E+1], rows [T*k], pos [T*k]) int32."""
+    _dev(topk_ids)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    cnt = torch.empty(E, dtype=torch.int32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    rows = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    pos = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    _check(library().moe_permute(_ptr(topk_ids), T, E, k, _ptr(cnt), _ptr(off), _ptr(rows), _ptr(pos),
+                                 _stream(stream)), "moe_permute")
+    return cnt, off, rows[:T * k], pos[:T * k]
+
+
+def moe_gate_up(x, Wgu, bgu, cnt, off, rows, k: int, path="auto", h=None, stream=None):
+    """Per-expert gate_up GEMM + bias + GLU; returns h (bf16 [T*k, I], permuted order)."""
+    _dev(x, Wgu, bgu, cnt, off, rows)
+    T, H = x.shape
+    E = Wgu.shape[0]
+    I = Wgu.shape[2] // 2
+    if h is None:
+        h = torch.empty((max(T * k, 1), I), dtype=torch.bfloat16, device=x.device)
+    _check(library().moe_gate_up(_ptr(x), _ptr(Wgu), _ptr(bgu), _ptr(cnt), _ptr(off), _ptr(rows), T, H, E,
+                                 k, I, _ptr(h), path_code(path), _stream(stream)), "moe_gate_up")
+    return h[:T * k]
+
+
+def moe_down(h, Wd, bd, cnt, off, T: int, k: int, path="auto", o=None, stream=None):
+    """Per-expert down GEMM + bias; returns o (float32 [T*k, H], permuted order)."""
+    _dev(h, Wd, bd, cnt, off)
+    E, I, H = Wd.shape
+    if o is None:
+        o = torch.empty((max(T * k, 1), H), dtype=torch.float32, device=h.device)
+    _check(library().moe_down(_ptr(h), _ptr(Wd), _ptr(bd), _ptr(cnt), _ptr(off), T, H, E, k, I, _ptr(o),
+                              path_code(path), _stream(stream)), "moe_down")
+    return o[:T * k]
+
+
+def moe_combine(o, pos, topk_w, y=None, stream=None):
+    """Weighted combine; returns y (bf16 [T, H])."""
+    _dev(o, pos, topk_w)
+    T, k = topk_w.shape
+    H = o.shape[1]
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=o.device)
+    _check(library().moe_combine(_ptr(o), _ptr(pos), _ptr(topk_w), T, H, k, _ptr(y), _stream(stream)),
+           "moe_combine")
+    return y

@@ -1,0 +1,50 @@
+// Routing-weighted combine of the k expert outputs of each token.
+//
+// xserv "Phase 19: gpt-oss-20b MoE support", section 2: the weighted sum takes
+// only the top-k experts of each token; experts a token did not select are
+// skipped (never multiplied by 0), so only the k selected rows of o are read.
+// The sum runs in float32 in the fixed order j = 0..k-1 and is rounded once to
+// bf16, so the result does not depend on launch order.
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const float* __restrict__ o, const int32_t* __restrict__ pos, const float* __restrict__ w,
+    int64_t T, int H, int k, bf16_t* __restrict__ y) {
+  // one thread per 4 consecutive columns of one token
+  const int64_t item = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
+  const int quads = H / 4;
+  if (item >= T * quads) return;   // no barrier in this kernel
+  const int64_t t = item / quads;
+  const int n = 4 * (int)(item - t * quads);
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const size_t s = (size_t)t * k + j;
+    const float wj = w[s];
+    const float4 v = *reinterpret_cast<const float4*>(o + (size_t)pos[s] * H + n);
+    a0 = fmaf(wj, v.x, a0);
+    a1 = fmaf(wj, v.y, a1);
+    a2 = fmaf(wj, v.z, a2);
+    a3 = fmaf(wj, v.w, a3);
+  }
+  u32x2_t out = {pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+  *reinterpret_cast<u32x2_t*>(y + (size_t)t * H + n) = out;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, int64_t T, int H, int k,
+                          void* y, hipStream_t stream) {
+  const int64_t items = T * (H / 4);
+  dim3 grid((unsigned)((items + kCombineThreads - 1) / kCombineThreads));
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, stream, o, pos, w, T, H, k,
+                     (bf16_t*)y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

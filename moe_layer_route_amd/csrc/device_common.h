@@ -1,0 +1,95 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;                                         // bfloat16 bit pattern
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));     // MFMA bf16 operand
+typedef float f32x4_t __attribute__((ext_vector_type(4)));       // 16x16 MFMA accumulator
+typedef float f32x16_t __attribute__((ext_vector_type(16)));     // 32x32 MFMA accumulator
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));    // 16-byte vector access
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+// low / high half of a packed pair of bf16
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float32 -> bfloat16, round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// v_perm_b32 byte selection over {hi:a, lo:b}
+__device__ __forceinline__ uint32_t perm_b32(uint32_t a, uint32_t b, uint32_t sel) {
+  return __builtin_amdgcn_perm(a, b, sel);
+}
+// (lo16 of x) | (lo16 of y) << 16
+__device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) { return perm_b32(y, x, 0x05040100u); }
+// (hi16 of x) | (hi16 of y) << 16
+__device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) { return perm_b32(y, x, 0x07060302u); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// 8x8 transpose of 16-bit elements held as 8 rows of u32x4_t (8 bf16 each):
+// out[j] holds column j of the input, element r in position r.
+__device__ __forceinline__ void transpose8x8_b16(const u32x4_t (&in)[8], u32x4_t (&out)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4_t& r0 = in[2 * q];
+      const u32x4_t& r1 = in[2 * q + 1];
+      uint32_t a, b;
+      switch (j >> 1) {
+        case 0: a = r0.x; b = r1.x; break;
+        case 1: a = r0.y; b = r1.y; break;
+        case 2: a = r0.z; b = r1.z; break;
+        default: a = r0.w; b = r1.w; break;
+      }
+      w[q] = (j & 1) ? pack_hi(a, b) : pack_lo(a, b);
+    }
+    out[j] = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// Clamped interleaved GLU of one (gate, up) pair, float32.
+__device__ __forceinline__ float clamped_glu(float gate, float up) {
+  const float g = fminf(gate, 7.0f);
+  const float u = fminf(fmaxf(up, -7.0f), 7.0f);
+  const float s = 1.0f / (1.0f + __expf(-1.702f * g));
+  return (u + 1.0f) * (g * s);
+}
+
+// streaming (read-once) 16-byte load
+__device__ __forceinline__ u32x4_t ldg16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+}  // namespace moe

@@ -1,0 +1,39 @@
+// Host-side launchers of the MoE block kernels (one per translation unit).
+// They only enqueue; argument validation happens in the C ABI (moe_abi.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define MOE_MAX_E_DEV 256
+#define MOE_MAX_K_DEV 8
+
+namespace moe {
+
+hipError_t launch_route(const void* x, const void* Wr, const void* br, int64_t T, int H, int E, int k,
+                        int32_t* ids, float* w, hipStream_t stream);
+
+hipError_t launch_permute(const int32_t* ids, int64_t T, int E, int k, int32_t* cnt, int32_t* off,
+                          int32_t* rows, int32_t* pos, hipStream_t stream);
+
+// Weight-streaming expert kernels (small token counts per expert).
+hipError_t launch_gemv_gate_up(const void* x, const void* Wgu, const void* bgu, const int32_t* cnt,
+                               const int32_t* off, const int32_t* rows, int H, int E, int k, int I,
+                               void* h, int max_rows_hint, hipStream_t stream);
+hipError_t launch_gemv_down(const void* h, const void* Wd, const void* bd, const int32_t* cnt,
+                            const int32_t* off, int H, int E, int I, float* o, int max_rows_hint,
+                            hipStream_t stream);
+
+// LDS-tiled MFMA grouped GEMMs (large token counts per expert).
+hipError_t launch_gemm_gate_up(const void* x, const void* Wgu, const void* bgu, const int32_t* cnt,
+                               const int32_t* off, const int32_t* rows, int64_t T, int H, int E, int k,
+                               int I, void* h, hipStream_t stream);
+hipError_t launch_gemm_down(const void* h, const void* Wd, const void* bd, const int32_t* cnt,
+                            const int32_t* off, int64_t T, int H, int E, int k, int I, float* o,
+                            hipStream_t stream);
+
+hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, int64_t T, int H, int k,
+                          void* y, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,277 @@
+// C ABI of the MoE block: host-side argument checks, workspace layout and the
+// per-call launch sequence.  Declared in include/moe_layer_route.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe_layer_route.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define CHECK_PTR(p, a)                                                                      \
+  do {                                                                                       \
+    if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);          \
+    if (!aligned((p), (a)))                                                                  \
+      return fail(MOE_ERR_INVALID_ARG, "%s: %s is not %d-byte aligned", fn, #p, (int)(a));  \
+  } while (0)
+
+int check_dims(const char* fn, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T=%lld < 0", fn, (long long)T);
+  if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", fn, E, MOE_MAX_E);
+  if (k < 1 || k > MOE_MAX_K || k > E)
+    return fail(MOE_ERR_INVALID_ARG, "%s: k=%d outside [1, min(E=%d, %d)]", fn, k, E, MOE_MAX_K);
+  if (H < 8 || H > MOE_MAX_DIM || H % 8 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: H=%d must be a multiple of 8 in [8, %d]", fn, H, MOE_MAX_DIM);
+  if (I < 8 || I > MOE_MAX_DIM || I % 8 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: I=%d must be a multiple of 8 in [8, %d]", fn, I, MOE_MAX_DIM);
+  if (T * (int64_t)k >= (int64_t)1 << 31)
+    return fail(MOE_ERR_INVALID_ARG, "%s: T*k=%lld must be below 2^31", fn, (long long)(T * k));
+  return MOE_OK;
+}
+
+int hip_status(const char* fn, hipError_t e) {
+  if (e == hipErrorNotSupported) return fail(MOE_ERR_UNSUPPORTED, "%s: path not implemented", fn);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+struct Layout {
+  size_t ids, w, cnt, off, rows, pos, h, o, total;
+};
+
+size_t take(size_t& cur, size_t bytes) {
+  const size_t at = cur;
+  cur += (bytes + 255) & ~(size_t)255;
+  return at;
+}
+
+Layout layout(int64_t T, int32_t H, int32_t E, int32_t k, int32_t I) {
+  Layout L;
+  size_t cur = 0;
+  const size_t S = (size_t)T * k;
+  L.ids = take(cur, S * 4);
+  L.w = take(cur, S * 4);
+  L.cnt = take(cur, (size_t)E * 4);
+  L.off = take(cur, (size_t)(E + 1) * 4);
+  L.rows = take(cur, S * 4);
+  L.pos = take(cur, S * 4);
+  L.h = take(cur, S * I * 2);
+  L.o = take(cur, S * H * 4);
+  L.total = cur;
+  return L;
+}
+
+// Expert path from host-known sizes only (no device read-back).
+int choose_path(int32_t path, int64_t T, int32_t E, int32_t k) {
+  if (path != MOE_PATH_AUTO) return path;
+  (void)T; (void)E; (void)k;
+  return MOE_PATH_GEMV;
+}
+
+int run_gate_up(const char* fn, const void* x, const void* Wgu, const void* bgu, const int32_t* cnt,
+                const int32_t* off, const int32_t* rows, int64_t T, int32_t H, int32_t E, int32_t k,
+                int32_t I, void* h, int32_t path, hipStream_t s) {
+  path = choose_path(path, T, E, k);
+  if (path == MOE_PATH_GEMV)
+    return hip_status(fn, moe::launch_gemv_gate_up(x, Wgu, bgu, cnt, off, rows, H, E, k, I, h,
+                                                   (int)((T * k + E - 1) / E), s));
+  if (path == MOE_PATH_GEMM)
+    return hip_status(fn, moe::launch_gemm_gate_up(x, Wgu, bgu, cnt, off, rows, T, H, E, k, I, h, s));
+  return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+}
+
+int run_down(const char* fn, const void* h, const void* Wd, const void* bd, const int32_t* cnt,
+             const int32_t* off, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, float* o,
+             int32_t path, hipStream_t s) {
+  path = choose_path(path, T, E, k);
+  if (path == MOE_PATH_GEMV)
+    return hip_status(fn, moe::launch_gemv_down(h, Wd, bd, cnt, off, H, E, I, o,
+                                                (int)((T * k + E - 1) / E), s));
+  if (path == MOE_PATH_GEMM)
+    return hip_status(fn, moe::launch_gemm_down(h, Wd, bd, cnt, off, T, H, E, k, I, o, s));
+  return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_workspace_bytes(int64_t T, int32_t H, int32_t E, int32_t k, int32_t I) {
+  if (check_dims("moe_workspace_bytes", T, H, E, k, I) != MOE_OK) return 0;
+  if (T == 0) return 0;
+  return layout(T, H, E, k, I).total;
+}
+
+int moe_route(const void* x, const void* Wr, const void* br, int64_t T, int32_t H, int32_t E, int32_t k,
+              int32_t* topk_ids, float* topk_w, void* stream) {
+  const char* fn = "moe_route";
+  // I only has to be valid for the shared check; the router does not use it.
+  if (int st = check_dims(fn, T, H, E, k, 8)) return st;
+  CHECK_PTR(x, 16);
+  CHECK_PTR(Wr, 16);
+  CHECK_PTR(br, 2);
+  CHECK_PTR(topk_ids, 4);
+  CHECK_PTR(topk_w, 4);
+  if (T == 0) return ok();
+  if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, topk_ids, topk_w,
+                                                (hipStream_t)stream)))
+    return st;
+  return ok();
+}
+
+int moe_forward_ex(const void* x, const void* Wr, const void* br, const void* Wgu, const void* bgu,
+                   const void* Wd, const void* bd, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                   void* y, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                   size_t workspace_bytes, int32_t path, void* stream) {
+  const char* fn = "moe_forward";
+  if (int st = check_dims(fn, T, H, E, k, I)) return st;
+  CHECK_PTR(x, 16);
+  CHECK_PTR(Wr, 16);
+  CHECK_PTR(br, 2);
+  CHECK_PTR(Wgu, 16);
+  CHECK_PTR(bgu, 4);
+  CHECK_PTR(Wd, 16);
+  CHECK_PTR(bd, 4);
+  CHECK_PTR(y, 16);
+  if (topk_ids_out && !aligned(topk_ids_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_ids_out is not 4-byte aligned", fn);
+  if (topk_w_out && !aligned(topk_w_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_w_out is not 4-byte aligned", fn);
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+  if (T == 0) return ok();
+  const Layout L = layout(T, H, E, k, I);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, L.total);
+  if (!aligned(workspace, 256))
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.cnt);
+  int32_t* off = reinterpret_cast<int32_t*>(ws + L.off);
+  int32_t* rows = reinterpret_cast<int32_t*>(ws + L.rows);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+  void* h = ws + L.h;
+  float* o = reinterpret_cast<float*>(ws + L.o);
+  hipStream_t s = (hipStream_t)stream;
+
+  if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, ids, w, s))) return st;
+  if (int st = hip_status(fn, moe::launch_permute(ids, T, E, k, cnt, off, rows, pos, s))) return st;
+  if (int st = run_gate_up(fn, x, Wgu, bgu, cnt, off, rows, T, H, E, k, I, h, path, s)) return st;
+  if (int st = run_down(fn, h, Wd, bd, cnt, off, T, H, E, k, I, o, path, s)) return st;
+  if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s))) return st;
+  return ok();
+}
+
+int moe_forward(const void* x, const void* Wr, const void* br, const void* Wgu, const void* bgu,
+                const void* Wd, const void* bd, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                void* y, int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  return moe_forward_ex(x, Wr, br, Wgu, bgu, Wd, bd, T, H, E, k, I, y, topk_ids_out, topk_w_out, workspace,
+                        workspace_bytes, MOE_PATH_AUTO, stream);
+}
+
+int moe_permute(const int32_t* topk_ids, int64_t T, int32_t E, int32_t k, int32_t* cnt, int32_t* off,
+                int32_t* rows, int32_t* pos, void* stream) {
+  const char* fn = "moe_permute";
+  if (int st = check_dims(fn, T, 8, E, k, 8)) return st;
+  CHECK_PTR(topk_ids, 4);
+  CHECK_PTR(cnt, 4);
+  CHECK_PTR(off, 4);
+  CHECK_PTR(rows, 4);
+  CHECK_PTR(pos, 4);
+  if (T == 0) return ok();
+  if (int st = hip_status(fn, moe::launch_permute(topk_ids, T, E, k, cnt, off, rows, pos,
+                                                  (hipStream_t)stream)))
+    return st;
+  return ok();
+}
+
+int moe_gate_up(const void* x, const void* Wgu, const void* bgu, const int32_t* cnt, const int32_t* off,
+                const int32_t* rows, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, void* h,
+                int32_t path, void* stream) {
+  const char* fn = "moe_gate_up";
+  if (int st = check_dims(fn, T, H, E, k, I)) return st;
+  CHECK_PTR(x, 16);
+  CHECK_PTR(Wgu, 16);
+  CHECK_PTR(bgu, 4);
+  CHECK_PTR(cnt, 4);
+  CHECK_PTR(off, 4);
+  CHECK_PTR(rows, 4);
+  CHECK_PTR(h, 16);
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+  if (T == 0) return ok();
+  if (int st = run_gate_up(fn, x, Wgu, bgu, cnt, off, rows, T, H, E, k, I, h, path, (hipStream_t)stream))
+    return st;
+  return ok();
+}
+
+int moe_down(const void* h, const void* Wd, const void* bd, const int32_t* cnt, const int32_t* off,
+             int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, float* o, int32_t path, void* stream) {
+  const char* fn = "moe_down";
+  if (int st = check_dims(fn, T, H, E, k, I)) return st;
+  CHECK_PTR(h, 16);
+  CHECK_PTR(Wd, 16);
+  CHECK_PTR(bd, 4);
+  CHECK_PTR(cnt, 4);
+  CHECK_PTR(off, 4);
+  CHECK_PTR(o, 16);
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+  if (T == 0) return ok();
+  if (int st = run_down(fn, h, Wd, bd, cnt, off, T, H, E, k, I, o, path, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int moe_combine(const float* o, const int32_t* pos, const float* topk_w, int64_t T, int32_t H, int32_t k,
+                void* y, void* stream) {
+  const char* fn = "moe_combine";
+  if (int st = check_dims(fn, T, H, MOE_MAX_E, k, 8)) return st;
+  CHECK_PTR(o, 16);
+  CHECK_PTR(pos, 4);
+  CHECK_PTR(topk_w, 4);
+  CHECK_PTR(y, 16);
+  if (T == 0) return ok();
+  if (int st = hip_status(fn, moe::launch_combine(o, pos, topk_w, T, H, k, y, (hipStream_t)stream)))
+    return st;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports every declared entry point and rejects bad
+arguments on the host before touching the GPU (CPU only: no call here
+reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_layer_route_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_layer_route.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+FAKE = 0x10000          # a 64 KiB-aligned non-null address that is never dereferenced
+
+
+def _declared():
+    src = open(HEADER).read()
+    return re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", src)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("library not built")
+    return binding.library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 11, names
+    raw = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_version_and_status_strings(lib):
+    ver = int(re.search(r"#define MOE_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.moe_abi_version() == ver
+    assert lib.moe_status_str(OK) == b"ok"
+    assert lib.moe_status_str(WORKSPACE) == b"workspace too small"
+    assert lib.moe_status_str(99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    for T, E in ((8, 32), (64, 32), (4096, 32), (256, 128), (16384, 128)):
+        n = lib.moe_workspace_bytes(T, 2880, E, 4, 2880)
+        S = T * 4
+        assert n >= S * 2880 * 2 + S * 2880 * 4 + 4 * S * 4 and n % 256 == 0
+    assert lib.moe_workspace_bytes(0, 2880, 32, 4, 2880) == 0
+    assert lib.moe_workspace_bytes(8, 2880, 4, 5, 2880) == 0            # k > E
+    assert b"k=5" in lib.moe_last_error()
+    assert lib.moe_workspace_bytes(8, 2884, 32, 4, 2880) == 0           # H % 8 != 0
+
+
+def _fwd(lib, T=8, H=64, E=8, k=2, I=64, ptrs=None, ws_bytes=1 << 30, path=0, ws=FAKE):
+    p = [FAKE] * 8 if ptrs is None else ptrs
+    return lib.moe_forward_ex(*[ctypes.c_void_p(v) if v else None for v in p[:7]], T, H, E, k, I,
+                              ctypes.c_void_p(p[7]) if p[7] else None, None, None,
+                              ctypes.c_void_p(ws) if ws else None, ws_bytes, path, None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(T=-1), "T=-1"), (dict(E=0), "E=0"), (dict(E=257), "E=257"), (dict(k=0), "k=0"),
+    (dict(k=9, E=16), "k=9"), (dict(k=5, E=4), "k=5"), (dict(H=60), "H=60"), (dict(I=12), "I=12"),
+    (dict(H=16392), "H=16392"), (dict(path=3), "path 3"), (dict(T=1 << 30, k=2), "T*k"),
+])
+def test_forward_rejects_bad_sizes(lib, kw, err):
+    assert _fwd(lib, **kw) == INVALID
+    assert err in lib.moe_last_error().decode()
+
+
+def test_forward_rejects_bad_pointers(lib):
+    for i in range(8):
+        p = [FAKE] * 8
+        p[i] = 0
+        assert _fwd(lib, ptrs=p) == INVALID
+        assert b"is NULL" in lib.moe_last_error()
+    p = [FAKE] * 8
+    p[0] = FAKE + 8                      # x must be 16-byte aligned
+    assert _fwd(lib, ptrs=p) == INVALID
+    assert b"aligned" in lib.moe_last_error()
+    assert _fwd(lib, ws=FAKE + 64) == INVALID        # workspace must be 256-byte aligned
+
+
+def test_forward_workspace_checks(lib):
+    need = lib.moe_workspace_bytes(8, 64, 8, 2, 64)
+    assert _fwd(lib, ws_bytes=need - 1) == WORKSPACE
+    assert _fwd(lib, ws=0) == WORKSPACE
+    assert b"needed" in lib.moe_last_error()
+
+
+def test_zero_tokens_is_a_no_op(lib):
+    assert _fwd(lib, T=0, ws=0, ws_bytes=0) == OK
+    assert lib.moe_last_error() == b""
+    v = ctypes.c_void_p(FAKE)
+    assert lib.moe_route(v, v, v, 0, 64, 8, 2, v, v, None) == OK
+    assert lib.moe_permute(v, 0, 8, 2, v, v, v, v, None) == OK
+    assert lib.moe_combine(v, v, v, 0, 64, 2, v, None) == OK
+
+
+def test_stage_calls_validate(lib):
+    v = ctypes.c_void_p(FAKE)
+    assert lib.moe_route(v, v, v, 4, 64, 8, 9, v, v, None) == INVALID
+    assert lib.moe_route(None, v, v, 4, 64, 8, 2, v, v, None) == INVALID
+    assert lib.moe_permute(v, 4, 300, 2, v, v, v, v, None) == INVALID
+    assert lib.moe_gate_up(v, v, v, v, v, v, 4, 64, 8, 2, 64, v, 7, None) == INVALID
+    assert lib.moe_down(v, v, v, v, None, 4, 64, 8, 2, 64, v, 0, None) == INVALID
+    assert lib.moe_combine(v, v, v, 4, 60, 2, v, None) == INVALID
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    mod = importlib.import_module("moe_layer_route_amd.binding")
+    saved = mod._lib
+    try:
+        mod._lib = None
+        with pytest.raises(binding.MoEError, match="not built"):
+            mod.library(str(tmp_path / "missing.so"))
+    finally:
+        mod._lib = saved
