@@ -109,6 +109,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy, the reference kernel "
+                         "that scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -128,6 +131,15 @@ def main(argv=None):
 
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("[bench] copy probe: 1 GiB read + 1 GiB written", file=sys.stderr, flush=True)
 
     x, Wr, br, Wgu, bgu, Wd, bd = [dev(a) for a in inp.arrays()]
     T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
@@ -163,8 +175,9 @@ def main(argv=None):
 
     def stage_step(ev=None):
         binding.moe_route(x, Wr, br, k, topk_ids=ids, topk_w=w, stream=stream)
-        binding.library().moe_permute(binding._ptr(ids), T, E, k, binding._ptr(cnt), binding._ptr(off),
-                                      binding._ptr(rows), binding._ptr(pos), binding._stream(stream))
+        st = binding.library().moe_permute(binding._ptr(ids), T, E, k, binding._ptr(cnt), binding._ptr(off),
+                                           binding._ptr(rows), binding._ptr(pos), binding._stream(stream))
+        binding._check(st, "moe_permute")
         if ev:
             ev[0].record(stream)
         binding.moe_gate_up(x, Wgu, bgu, cnt, off, rows, k, path=args.path, h=h, stream=stream)
