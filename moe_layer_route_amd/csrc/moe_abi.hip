@@ -79,11 +79,15 @@ Layout layout(int64_t T, int32_t H, int32_t E, int32_t k, int32_t I) {
   return L;
 }
 
-// Expert path from host-known sizes only (no device read-back).
+// Mean rows per expert above which the tiled MFMA path is used.
+constexpr int64_t kGemmMinMeanRows = 48;
+
+// Expert path from host-known sizes only (no device read-back): the weight
+// streaming path while each expert sees few rows, the tiled MFMA path once the
+// mean load per expert makes the GEMMs compute-bound.
 int choose_path(int32_t path, int64_t T, int32_t E, int32_t k) {
   if (path != MOE_PATH_AUTO) return path;
-  (void)T; (void)E; (void)k;
-  return MOE_PATH_GEMV;
+  return T * k > kGemmMinMeanRows * E ? MOE_PATH_GEMM : MOE_PATH_GEMV;
 }
 
 int run_gate_up(const char* fn, const void* x, const void* Wgu, const void* bgu, const int32_t* cnt,
