@@ -195,10 +195,20 @@ def main(argv=None):
     gate_up_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     D = int((torch.bincount(ids.reshape(-1).long(), minlength=E) > 0).sum().item())
+    path = args.path if args.path != "auto" else binding.expert_path(T, E, k)
     gu_bytes = _alg_bytes_gate_up(cfg, D)
-    achieved = gu_bytes / (gate_up_ms * 1e-3) / 1e9
-    gu_file = "moe_layer_route_amd/csrc/gemv.hip"
+    gu_flops = 2 * T * k * H * 2 * I
+    gu_file = f"moe_layer_route_amd/csrc/{path}.hip"
     traffic = _traffic(gu_file, cfg.name)
+    if path == "gemv":
+        roofline = {"bound": "hbm", "kernel": "gemv_expert_kernel<gate_up>",
+                    "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roofline = {"bound": "mfma", "kernel": "gemm_expert_kernel<gate_up>",
+                    "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s"}
+    roofline.update(frac=roofline["achieved"] / roofline["peak"], traffic=traffic,
+                    alg_bytes_per_launch=gu_bytes, alg_flops_per_launch=gu_flops, launch_us=gate_up_ms * 1e3)
     layer_bytes = _alg_bytes_layer(cfg, D)
     layer_flops = _alg_flops_layer(cfg)
     step_s = ms_per_step * 1e-3
@@ -217,10 +227,8 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic (seeded normal bf16 inputs of the gpt-oss MoE block shapes; random-init weights)",
         "config": {"workload": f"{cfg.name}: {cfg.description}", "T": T, "H": H, "I": I, "E": E, "k": k,
-                   "seed": 0, "path": args.path, "live_experts": D},
-        "roofline": {"bound": "hbm", "kernel": "gemv_expert_kernel<gate_up>", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "alg_bytes_per_launch": gu_bytes, "launch_us": gate_up_ms * 1e3},
+                   "seed": 0, "path": path, "live_experts": D},
+        "roofline": roofline,
         "layer": {"alg_bytes": layer_bytes, "alg_flops": layer_flops,
                   "hbm_GBs": layer_bytes / step_s / 1e9, "hbm_frac": layer_bytes / step_s / 1e9 / HBM_PEAK_GBS,
                   "tflops": layer_flops / step_s / 1e12,

@@ -89,6 +89,10 @@ MOE_API const char* moe_last_error(void);
  */
 MOE_API size_t moe_workspace_bytes(int64_t T, int32_t H, int32_t E, int32_t k, int32_t I);
 
+/* The expert path (MOE_PATH_GEMV or MOE_PATH_GEMM) that MOE_PATH_AUTO takes
+ * for these sizes; it depends on T, E and k only (mean rows per expert). */
+MOE_API int moe_expert_path(int64_t T, int32_t E, int32_t k);
+
 /*
  * moe_route -- router logits, top-k and softmax weights
  * (architecture table "MoE" row; forward pipeline, first two steps).

@@ -10,7 +10,7 @@ native library, so ``import moe_layer_route_amd.datagen`` works without it.
 from __future__ import annotations
 
 __all__ = ["moe_route", "moe_forward", "moe_forward_ex", "moe_permute", "moe_gate_up",
-           "moe_down", "moe_combine", "workspace_bytes", "library", "MoEError"]
+           "moe_down", "moe_combine", "workspace_bytes", "expert_path", "library", "MoEError"]
 
 
 def __getattr__(name):

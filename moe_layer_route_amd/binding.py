@@ -18,7 +18,8 @@ _PATHS = {"auto": PATH_AUTO, "gemv": PATH_GEMV, "gemm": PATH_GEMM}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_layer_route.so")
 
-EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace_bytes", "moe_route",
+EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace_bytes", "moe_expert_path",
+           "moe_route",
            "moe_forward", "moe_forward_ex", "moe_permute", "moe_gate_up", "moe_down", "moe_combine")
 
 
@@ -34,6 +35,7 @@ _SIGS = {
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32]),
+    "moe_expert_path": (ctypes.c_int, [_i64, _i32, _i32]),
     "moe_route": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
     "moe_forward": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _vp]),
     "moe_forward_ex": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _i32, _vp]),
@@ -97,6 +99,11 @@ def path_code(path) -> int:
     if isinstance(path, str):
         return _PATHS[path]
     return int(path)
+
+
+def expert_path(T: int, E: int, k: int) -> str:
+    """The expert path ("gemv" or "gemm") the library picks for these sizes."""
+    return {PATH_GEMV: "gemv", PATH_GEMM: "gemm"}[int(library().moe_expert_path(T, E, k))]
 
 
 def workspace_bytes(T: int, H: int, E: int, k: int, I: int) -> int:

@@ -133,6 +133,8 @@ const char* moe_status_str(int status) {
 
 const char* moe_last_error(void) { return g_err; }
 
+int moe_expert_path(int64_t T, int32_t E, int32_t k) { return choose_path(MOE_PATH_AUTO, T, E, k); }
+
 size_t moe_workspace_bytes(int64_t T, int32_t H, int32_t E, int32_t k, int32_t I) {
   if (check_dims("moe_workspace_bytes", T, H, E, k, I) != MOE_OK) return 0;
   if (T == 0) return 0;
