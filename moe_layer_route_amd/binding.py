@@ -16,7 +16,9 @@ import torch
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
 _PATHS = {"auto": PATH_AUTO, "gemv": PATH_GEMV, "gemm": PATH_GEMM}
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_layer_route.so")
+# The in-tree build; MOE_LAYER_ROUTE_LIB may name another build of the same library.
+LIB_PATH = os.environ.get("MOE_LAYER_ROUTE_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe_layer_route.so")
 
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace_bytes", "moe_expert_path",
            "moe_route",

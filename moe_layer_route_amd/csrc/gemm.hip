@@ -10,39 +10,44 @@
 // only: (number of N tiles) x (an upper bound on the M tiles of all experts,
 // ceil(T*k / BM) + E).  Each workgroup looks up which expert and which rows its
 // M-tile slot holds from cnt[] (prefix sum of ceil(cnt[e] / BM)); surplus
-// slots exit before any load.  Linear block ids are remapped so that
-// consecutive tiles (the M tiles of one expert on one N tile, which share the
-// weight slab) land on the same XCD, whose L2 then serves the reuse.
+// slots exit before any load or barrier.  Linear block ids are remapped so
+// that consecutive tiles (the M tiles of one expert on one N tile, which share
+// the weight slab) run on the same XCD, whose L2 serves the reuse.
 //
-// Tile: BM x 256 output, K steps of 32, 4 waves in a 2 x 2 layout, each wave
-// BM/2 x 128 with v_mfma_f32_32x32x16_bf16.  Both operands are staged in LDS
-// as [row][k] with k contiguous (rows padded to 80 bytes, conflict-free
-// 16-byte reads), double buffered with one barrier per K step:
-//   A: token rows, gathered through rows[] (gate_up) or contiguous rows of h
-//      (down), copied 16 bytes at a time;
-//   B: the weight is stored [K][N] (N contiguous), so each thread loads a 4 x 8
-//      block (4 k rows, 8 columns) and transposes it in registers into eight
-//      4-element k runs, one per column.  For gate_up the columns are also
-//      de-interleaved on the way into LDS: within every 64 columns, the 32
-//      gate columns (even) come first and the 32 up columns (odd) second, so
-//      MFMA tiles 2q and 2q+1 of a wave hold the gate and the up value of the
-//      same (row, pair) in the same lane and the GLU epilogue is lane-local.
+// Tile: 128 rows x 512 columns, K steps of 32, eight waves (two per SIMD)
+// side by side along N; each owns 128 rows x 64 columns = 8 x 4 tiles of
+// v_mfma_f32_16x16x32_bf16 (128 fp32 accumulators per lane).
+//   B (weight, [K][N] with N contiguous): no two waves share a column, so B
+//     bypasses LDS.  Lane (g = lane/16, c = lane%16) of a wave loads rows
+//     k0+8g .. k0+8g+7 of its 4 columns c0+4c .. c0+4c+3 (8-byte buffer loads,
+//     two K steps ahead); an 8x4 transpose in registers turns them into four
+//     K-packed B operands: operand j holds column c0+4c+j in MFMA column c.
+//   A (token rows, k contiguous) is shared by the eight waves: gathered
+//     through rows[] (gate_up) or contiguous rows of h (down), staged through
+//     registers into two LDS buffers, one barrier per K step.  The buffers are
+//     fragment-major: fragment mi (rows 16 mi .. 16 mi + 15) is 1 KB holding,
+//     in lane order, the 16 bytes lane l of the MFMA needs (row l%16, k chunk
+//     l/16), so every fragment read and every store is one contiguous 1 KB
+//     access, free of bank conflicts.
+// Epilogue: in the 16x16 accumulator layout lane l holds rows 4*(l/16)+0..3
+// of MFMA column l%16, i.e. weight column c0+4c+j of operand j, so gate
+// (j even) and up (j+1) of one pair sit in the same lane: bias + clamped GLU
+// in registers, h stored as bf16 (gate_up); bias and float32 store (down).
 #include "device_common.h"
 #include "launch.h"
 
 namespace moe {
 namespace {
 
-constexpr int kGmThreads = 256;
-constexpr int kGmBN = 256;
+constexpr int kGmThreads = 512;
+constexpr int kGmBM = 128;
+constexpr int kGmBN = 512;
 constexpr int kGmBK = 32;
-constexpr int kGmLd = kGmBK + 8;   // LDS row pitch in bf16 (80 bytes)
 constexpr int kXcds = 8;
 
-template <int BM>
+
 struct GemmSmem {
-  bf16_t a[2][BM][kGmLd];
-  bf16_t b[2][kGmBN][kGmLd];
+  u32x4_t a[2][kGmBM / 16][kWave];   // 2 x 8 fragments x 1 KB
 };
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -54,20 +59,34 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-template <int BM, bool GATE_UP>
-__global__ __launch_bounds__(kGmThreads, 2) void gemm_expert_kernel(
+struct Stage {
+  u32x4_t a;
+  u32x2_t b[8];
+};
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer descriptor over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ u32x2_t buf_ld8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(kGmThreads, 1) void gemm_expert_kernel(
     const bf16_t* __restrict__ A,      // gate_up: x [T][K]; down: h [S][K] (permuted order)
     const bf16_t* __restrict__ W,      // [E][K][N]
     const bf16_t* __restrict__ bias,   // [E][N]
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ off,
     const int32_t* __restrict__ rows,  // gate_up: permuted slot ids
-    int K, int N, int E, int kslots, int n_tiles, int m_slots, void* __restrict__ out) {
-  __shared__ __align__(16) GemmSmem<BM> sm;
+    int K, int N, int E, int kslots, int a_rows, int n_tiles, int m_slots, void* __restrict__ out) {
+  __shared__ __align__(16) GemmSmem sm;
   __shared__ int s_tile[2];
-
-  constexpr int MI = BM / 64;          // 32-row MFMA tiles per wave along M
-  constexpr int NI = 4;                // 32-column MFMA tiles per wave along N
-  constexpr int A_CHUNKS = BM * (kGmBK / 8) / kGmThreads;   // 16-byte A chunks per thread
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -88,7 +107,7 @@ __global__ __launch_bounds__(kGmThreads, 2) void gemm_expert_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane * 4 + i;
-      tc[i] = e < E ? (cnt[e] + BM - 1) / BM : 0;
+      tc[i] = e < E ? (cnt[e] + kGmBM - 1) / kGmBM : 0;
       sum += tc[i];
     }
     int start = wave_incl_scan(sum, lane) - sum;
@@ -96,7 +115,7 @@ __global__ __launch_bounds__(kGmThreads, 2) void gemm_expert_kernel(
     for (int i = 0; i < 4; ++i) {
       if (ms >= start && ms < start + tc[i]) {
         s_tile[0] = lane * 4 + i;
-        s_tile[1] = (ms - start) * BM;
+        s_tile[1] = (ms - start) * kGmBM;
       }
       start += tc[i];
     }
@@ -110,154 +129,145 @@ __global__ __launch_bounds__(kGmThreads, 2) void gemm_expert_kernel(
   const int n0 = nt * kGmBN;
 
   // ---- per-thread global load assignments ----
-  const bf16_t* a_ptr[A_CHUNKS];
-  bool a_ok[A_CHUNKS];
-  int a_row[A_CHUNKS], a_kc[A_CHUNKS];
-#pragma unroll
-  for (int i = 0; i < A_CHUNKS; ++i) {
-    const int c = tid + kGmThreads * i;
-    a_row[i] = c >> 2;
-    a_kc[i] = c & 3;
-    const int m = m0 + a_row[i];
-    a_ok[i] = m < M;
-    size_t r = 0;
-    if (a_ok[i]) r = GATE_UP ? (size_t)(rows[row0 + m] / kslots) : (size_t)(row0 + m);
-    a_ptr[i] = A + r * K + 8 * a_kc[i];
+  // Buffer loads: the descriptor (SGPRs) holds the base, each lane a constant
+  // 32-bit offset, and the K step advances a uniform offset, which keeps the
+  // VGPRs free for three stages of loads in flight.  Every load is
+  // unconditional (a masked load becomes a branch, and the compiler then
+  // drains all outstanding loads at the merge).  Rows past M and columns past
+  // N read a valid row/column instead: they only feed outputs that are never
+  // stored.  K-tail reads fall outside the descriptor's range and return 0.
+  // A: thread t copies the 16 bytes lane t%64 of fragment t/64 holds: row
+  // 16 (t/64) + t%16, k chunk (t/16)%4
+  const rsrc_t a_rs = make_rsrc(A, (uint32_t)((size_t)a_rows * K * 2));
+  const int a_row = 16 * wave + (lane & 15);
+  const int a_kc = lane >> 4;
+  uint32_t a_off;
+  {
+    const int m = min(m0 + a_row, M - 1);
+    const uint32_t r = GATE_UP ? (uint32_t)(rows[row0 + m] / kslots) : (uint32_t)(row0 + m);
+    a_off = (r * (uint32_t)K + 8u * a_kc) * 2u;
   }
-  const int b_kq = tid >> 5;          // 4-row group of the K step (0..7)
-  const int b_nb = tid & 31;          // 8-column group of the N tile (0..31)
-  const bool b_ok = n0 + 8 * b_nb < N;
-  const bf16_t* b_ptr = W + (size_t)e * K * N + (size_t)(4 * b_kq) * N + n0 + 8 * b_nb;
-  int b_lrow[8];                      // LDS row of each of the thread's 8 columns
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int pc = 8 * b_nb + j;
-    b_lrow[j] = GATE_UP ? 64 * (pc >> 6) + 32 * (pc & 1) + ((pc & 63) >> 1) : pc;
-  }
+  // B: lane (g, c) of wave w reads rows k0 + 8g + r (r = 0..7) of the 8-byte
+  // piece at column n0 + 64 w + 4c
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const rsrc_t b_rs = make_rsrc(W + (size_t)e * K * N, (uint32_t)((size_t)K * N * 2));
+  const int b_gcol = n0 + wave * 64 + 4 * c;
+  const uint32_t b_off = ((uint32_t)(8 * g) * N + (uint32_t)min(b_gcol, N - 4)) * 2u;
 
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-  u32x4_t ra[A_CHUNKS], rb[4];
-  auto load_global = [&](int kt) {
+  auto gload = [&](int kt, Stage& st) {
     const int k0 = kt * kGmBK;
+    const bool ok = k0 + 8 * a_kc < K;
+    st.a = buf_ld16(a_rs, ok ? a_off + 2u * k0 : 0xFFFFFFF0u, 0);
+    const uint32_t soff = (uint32_t)k0 * N * 2u;
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i)
-      ra[i] = (a_ok[i] && k0 + 8 * a_kc[i] < K) ? ld16(a_ptr[i] + k0) : zero;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      rb[r] = (b_ok && k0 + 4 * b_kq + r < K) ? ldg16_stream(b_ptr + (size_t)(k0 + r) * N) : zero;
+    for (int r = 0; r < 8; ++r) st.b[r] = buf_ld8(b_rs, b_off + (uint32_t)r * N * 2u, soff);
   };
-  auto store_lds = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i)
-      *reinterpret_cast<u32x4_t*>(&sm.a[buf][a_row[i]][8 * a_kc[i]]) = ra[i];
-    // 4 x 8 transpose: column j becomes the k run (r0[j], r1[j], r2[j], r3[j])
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = j >> 1;
-      const uint32_t w0 = rb[0][d], w1 = rb[1][d], w2 = rb[2][d], w3 = rb[3][d];
-      u32x2_t v;
-      v[0] = (j & 1) ? pack_hi(w0, w1) : pack_lo(w0, w1);
-      v[1] = (j & 1) ? pack_hi(w2, w3) : pack_lo(w2, w3);
-      *reinterpret_cast<u32x2_t*>(&sm.b[buf][b_lrow[j]][4 * b_kq]) = v;
-    }
-  };
+  auto lstore = [&](int buf, const Stage& st) { sm.a[buf][wave][lane] = st.a; };
 
-  f32x16_t acc[MI][NI];
+  f32x4_t acc[8][4];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+    for (int j = 0; j < 4; ++j) acc[mi][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int frag_row = lane & 31;
-  const int frag_k = 8 * (lane >> 5);
-  const int nk = (K + kGmBK - 1) / kGmBK;
-
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_global(kt + 1);
+  auto compute = [&](int buf, const Stage& st) {
+    // 8 x 4 transpose: operand j, dword q = (row 2q, row 2q+1) of column j
+    u32x4_t bt[4];
 #pragma unroll
-    for (int ks = 0; ks < kGmBK / 16; ++ks) {
-      u32x4_t af[MI], bfr[NI];
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w[4];
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        af[mi] = *reinterpret_cast<const u32x4_t*>(
-            &sm.a[buf][wm * (BM / 2) + mi * 32 + frag_row][ks * 16 + frag_k]);
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        bfr[ni] = *reinterpret_cast<const u32x4_t*>(
-            &sm.b[buf][wn * 128 + ni * 32 + frag_row][ks * 16 + frag_k]);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32x32x16(af[mi], bfr[ni], acc[mi][ni]);
-    }
-    if (kt + 1 < nk) store_lds(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue.  32x32 accumulator layout: lane l, element v holds
-  // row 8*(v/4) + 4*(l/32) + v%4, column l%32 of the MFMA tile. ----
-  const int col = lane & 31;
-  const int rq = 4 * (lane >> 5);
-  if (GATE_UP) {
-    const int I = N / 2;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int i = n0 / 2 + wn * 64 + q * 32 + col;     // h column (gate/up pair)
-      const bool i_ok = i < I;
-      float bg = 0.f, bu = 0.f;
-      if (i_ok) {
-        const uint32_t bw = *reinterpret_cast<const uint32_t*>(bias + (size_t)e * N + 2 * i);
-        bg = bf16lo(bw);
-        bu = bf16hi(bw);
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t x0 = st.b[2 * q][j >> 1], x1 = st.b[2 * q + 1][j >> 1];
+        w[q] = (j & 1) ? pack_hi(x0, x1) : pack_lo(x0, x1);
       }
+      bt[j] = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < 8; ++mi) {
+      const u32x4_t af = sm.a[buf][mi][lane];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = m0 + wm * (BM / 2) + mi * 32 + 8 * (v >> 2) + rq + (v & 3);
-          if (i_ok && m < M) {
-            const float hv = clamped_glu(acc[mi][2 * q][v] + bg, acc[mi][2 * q + 1][v] + bu);
-            reinterpret_cast<uint16_t*>(out)[(size_t)(row0 + m) * I + i] = (uint16_t)f32_to_bf16(hv);
+      for (int j = 0; j < 4; ++j) acc[mi][j] = mfma16x16x32(af, bt[j], acc[mi][j]);
+    }
+  };
+
+  const int nk = (K + kGmBK - 1) / kGmBK;
+  Stage R0, R1, R2;
+  gload(0, R0);
+  gload(1, R1);
+  lstore(0, R0);
+  __syncthreads();
+  // One K step: issue the loads two steps ahead, multiply the current step
+  // (A from LDS, B from registers), move the next step's A into the other LDS
+  // buffer.  Prefetch and store are unconditional: loads past K return 0 from
+  // the buffer descriptors and land where nobody reads them, and a conditional
+  // load would make the compiler wait for every outstanding load.
+  // The scheduling fences keep the transpose of a stage inside its own step:
+  // hoisted next to the loads it reads, it would force a wait on them.
+  auto step = [&](int kt, const Stage& cur, const Stage& next, Stage& ahead) {
+    gload(kt + 2, ahead);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kt & 1, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    lstore((kt + 1) & 1, next);
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {
+    step(kt, R0, R1, R2);
+    step(kt + 1, R1, R2, R0);
+    step(kt + 2, R2, R0, R1);
+  }
+  if (kt < nk) step(kt, R0, R1, R2);
+  if (kt + 1 < nk) step(kt + 1, R1, R2, R0);
+
+  // ---- epilogue.  16x16 accumulator layout: lane l, element v holds row
+  // 4*(l/16) + v of MFMA column l%16 = weight column b_gcol + j of operand j.
+#pragma unroll
+  for (int j = 0; j < 4; j += 2) {
+    const int n = b_gcol + j;
+    const bool n_ok = n < N;
+    float b0 = 0.f, b1 = 0.f;
+    if (n_ok) {
+      const uint32_t bw = *reinterpret_cast<const uint32_t*>(bias + (size_t)e * N + n);
+      b0 = bf16lo(bw);
+      b1 = bf16hi(bw);
+    }
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + mi * 16 + 4 * g + v;
+        if (n_ok && m < M) {
+          if (GATE_UP) {
+            const float hv = clamped_glu(acc[mi][j][v] + b0, acc[mi][j + 1][v] + b1);
+            reinterpret_cast<uint16_t*>(out)[(size_t)(row0 + m) * (N / 2) + n / 2] = (uint16_t)f32_to_bf16(hv);
+          } else {
+            *reinterpret_cast<float2*>(reinterpret_cast<float*>(out) + (size_t)(row0 + m) * N + n) =
+                make_float2(acc[mi][j][v] + b0, acc[mi][j + 1][v] + b1);
           }
         }
-    }
-  } else {
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      const int n = n0 + wn * 128 + ni * 32 + col;
-      const bool n_ok = n < N;
-      const float bv = n_ok ? bf16_to_f32(bias[(size_t)e * N + n]) : 0.f;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = m0 + wm * (BM / 2) + mi * 32 + 8 * (v >> 2) + rq + (v & 3);
-          if (n_ok && m < M) reinterpret_cast<float*>(out)[(size_t)(row0 + m) * N + n] = acc[mi][ni][v] + bv;
-        }
-    }
+      }
   }
 }
 
-template <int BM, bool GATE_UP>
+template <bool GATE_UP>
 hipError_t launch(const void* A, const void* W, const void* bias, const int32_t* cnt, const int32_t* off,
                   const int32_t* rows, int64_t T, int K, int N, int E, int k, void* out, hipStream_t stream) {
   const int64_t S = T * k;
+  const int64_t a_rows = GATE_UP ? T : S;
+  // 32-bit buffer offsets: one operand (or one expert's weight) below 4 GiB
+  if (a_rows * K * 2 >= ((int64_t)1 << 32) || (int64_t)K * N * 2 >= ((int64_t)1 << 32))
+    return hipErrorNotSupported;
   const int n_tiles = (N + kGmBN - 1) / kGmBN;
-  const int64_t m_slots = (S + BM - 1) / BM + E;
+  const int64_t m_slots = (S + kGmBM - 1) / kGmBM + E;
   const int64_t blocks = (int64_t)n_tiles * m_slots;
   const int64_t grid = (blocks + kXcds - 1) / kXcds * kXcds;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_expert_kernel<BM, GATE_UP>), dim3((unsigned)grid), dim3(kGmThreads), 0, stream,
+  hipLaunchKernelGGL((gemm_expert_kernel<GATE_UP>), dim3((unsigned)grid), dim3(kGmThreads), 0, stream,
                      (const bf16_t*)A, (const bf16_t*)W, (const bf16_t*)bias, cnt, off, rows, K, N, E, k,
-                     n_tiles, (int)m_slots, out);
+                     (int)a_rows, n_tiles, (int)m_slots, out);
   return hipGetLastError();
 }
 
@@ -266,13 +276,13 @@ hipError_t launch(const void* A, const void* W, const void* bias, const int32_t*
 hipError_t launch_gemm_gate_up(const void* x, const void* Wgu, const void* bgu, const int32_t* cnt,
                                const int32_t* off, const int32_t* rows, int64_t T, int H, int E, int k,
                                int I, void* h, hipStream_t stream) {
-  return launch<128, true>(x, Wgu, bgu, cnt, off, rows, T, H, 2 * I, E, k, h, stream);
+  return launch<true>(x, Wgu, bgu, cnt, off, rows, T, H, 2 * I, E, k, h, stream);
 }
 
 hipError_t launch_gemm_down(const void* h, const void* Wd, const void* bd, const int32_t* cnt,
                             const int32_t* off, int64_t T, int H, int E, int k, int I, float* o,
                             hipStream_t stream) {
-  return launch<128, false>(h, Wd, bd, cnt, off, nullptr, T, I, H, E, k, o, stream);
+  return launch<false>(h, Wd, bd, cnt, off, nullptr, T, I, H, E, k, o, stream);
 }
 
 }  // namespace moe
