@@ -114,6 +114,19 @@ MOE_API int moe_route(const void* x, const void* Wr, const void* br,
               int64_t T, int32_t H, int32_t E, int32_t k,
               int32_t* topk_ids, float* topk_w, void* stream);
 
+/* Router methods of moe_route_ex. */
+#define MOE_ROUTE_AUTO 0    /* exact below 64K logits (T*E), MFMA + refinement above */
+#define MOE_ROUTE_EXACT 1   /* every logit as an exact-product float64 sum */
+#define MOE_ROUTE_MFMA 2    /* bf16 MFMA logits with error bounds; ties near the top k
+                               recomputed exactly; same decision as MOE_ROUTE_EXACT */
+
+/* moe_route with the router method forced (MOE_ROUTE_*); both methods give
+ * the same topk_ids (and topk_w within 1e-6), so the choice only affects speed.
+ * moe_route is moe_route_ex(..., MOE_ROUTE_AUTO, stream). */
+MOE_API int moe_route_ex(const void* x, const void* Wr, const void* br,
+                         int64_t T, int32_t H, int32_t E, int32_t k,
+                         int32_t* topk_ids, float* topk_w, int32_t method, void* stream);
+
 /*
  * moe_forward -- the whole MoE block forward (forward pipeline, all steps).
  *

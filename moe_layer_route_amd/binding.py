@@ -15,13 +15,15 @@ import torch
 
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
 _PATHS = {"auto": PATH_AUTO, "gemv": PATH_GEMV, "gemm": PATH_GEMM}
+ROUTE_AUTO, ROUTE_EXACT, ROUTE_MFMA = 0, 1, 2
+_ROUTES = {"auto": ROUTE_AUTO, "exact": ROUTE_EXACT, "mfma": ROUTE_MFMA}
 
 # The in-tree build; MOE_LAYER_ROUTE_LIB may name another build of the same library.
 LIB_PATH = os.environ.get("MOE_LAYER_ROUTE_LIB") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libmoe_layer_route.so")
 
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace_bytes", "moe_expert_path",
-           "moe_route",
+           "moe_route", "moe_route_ex",
            "moe_forward", "moe_forward_ex", "moe_permute", "moe_gate_up", "moe_down", "moe_combine")
 
 
@@ -39,6 +41,7 @@ _SIGS = {
     "moe_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32]),
     "moe_expert_path": (ctypes.c_int, [_i64, _i32, _i32]),
     "moe_route": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "moe_route_ex": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _i32, _vp]),
     "moe_forward": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _vp]),
     "moe_forward_ex": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _i32, _vp]),
     "moe_permute": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
@@ -117,8 +120,10 @@ def alloc_workspace(T: int, H: int, E: int, k: int, I: int, device=None) -> torc
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device or "cuda")
 
 
-def moe_route(x, Wr, br, k: int, topk_ids=None, topk_w=None, stream=None):
-    """Router: returns (topk_ids int32 [T,k], topk_w float32 [T,k])."""
+def moe_route(x, Wr, br, k: int, topk_ids=None, topk_w=None, method="auto", stream=None):
+    """Router: returns (topk_ids int32 [T,k], topk_w float32 [T,k]).
+
+    method: "auto", "exact" or "mfma" (same decision; speed only)."""
     _dev(x, Wr, br)
     _b16(x, Wr, br)
     T, H = x.shape
@@ -128,8 +133,9 @@ def moe_route(x, Wr, br, k: int, topk_ids=None, topk_w=None, stream=None):
     if topk_w is None:
         topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     _dev(topk_ids, topk_w)
-    _check(library().moe_route(_ptr(x), _ptr(Wr), _ptr(br), T, H, E, k, _ptr(topk_ids), _ptr(topk_w),
-                               _stream(stream)), "moe_route")
+    m = _ROUTES[method] if isinstance(method, str) else int(method)
+    _check(library().moe_route_ex(_ptr(x), _ptr(Wr), _ptr(br), T, H, E, k, _ptr(topk_ids), _ptr(topk_w), m,
+                                  _stream(stream)), "moe_route")
     return topk_ids, topk_w
 
 

@@ -11,8 +11,9 @@
 
 namespace moe {
 
+// method: 0 = by size, 1 = exact float64 kernel, 2 = MFMA kernel with exact refinement
 hipError_t launch_route(const void* x, const void* Wr, const void* br, int64_t T, int H, int E, int k,
-                        int32_t* ids, float* w, hipStream_t stream);
+                        int32_t* ids, float* w, int method, hipStream_t stream);
 
 hipError_t launch_permute(const int32_t* ids, int64_t T, int E, int k, int32_t* cnt, int32_t* off,
                           int32_t* rows, int32_t* pos, hipStream_t stream);

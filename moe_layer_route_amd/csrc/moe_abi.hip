@@ -141,8 +141,8 @@ size_t moe_workspace_bytes(int64_t T, int32_t H, int32_t E, int32_t k, int32_t I
   return layout(T, H, E, k, I).total;
 }
 
-int moe_route(const void* x, const void* Wr, const void* br, int64_t T, int32_t H, int32_t E, int32_t k,
-              int32_t* topk_ids, float* topk_w, void* stream) {
+int moe_route_ex(const void* x, const void* Wr, const void* br, int64_t T, int32_t H, int32_t E, int32_t k,
+                 int32_t* topk_ids, float* topk_w, int32_t method, void* stream) {
   const char* fn = "moe_route";
   // I only has to be valid for the shared check; the router does not use it.
   if (int st = check_dims(fn, T, H, E, k, 8)) return st;
@@ -151,11 +151,18 @@ int moe_route(const void* x, const void* Wr, const void* br, int64_t T, int32_t 
   CHECK_PTR(br, 2);
   CHECK_PTR(topk_ids, 4);
   CHECK_PTR(topk_w, 4);
+  if (method < MOE_ROUTE_AUTO || method > MOE_ROUTE_MFMA)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown router method %d", fn, method);
   if (T == 0) return ok();
-  if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, topk_ids, topk_w,
+  if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, topk_ids, topk_w, method,
                                                 (hipStream_t)stream)))
     return st;
   return ok();
+}
+
+int moe_route(const void* x, const void* Wr, const void* br, int64_t T, int32_t H, int32_t E, int32_t k,
+              int32_t* topk_ids, float* topk_w, void* stream) {
+  return moe_route_ex(x, Wr, br, T, H, E, k, topk_ids, topk_w, MOE_ROUTE_AUTO, stream);
 }
 
 int moe_forward_ex(const void* x, const void* Wr, const void* br, const void* Wgu, const void* bgu,
@@ -197,7 +204,7 @@ int moe_forward_ex(const void* x, const void* Wr, const void* br, const void* Wg
   float* o = reinterpret_cast<float*>(ws + L.o);
   hipStream_t s = (hipStream_t)stream;
 
-  if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, ids, w, s))) return st;
+  if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, ids, w, MOE_ROUTE_AUTO, s))) return st;
   if (int st = hip_status(fn, moe::launch_permute(ids, T, E, k, cnt, off, rows, pos, s))) return st;
   if (int st = run_gate_up(fn, x, Wgu, bgu, cnt, off, rows, T, H, E, k, I, h, path, s)) return st;
   if (int st = run_down(fn, h, Wd, bd, cnt, off, T, H, E, k, I, o, path, s)) return st;

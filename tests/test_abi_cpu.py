@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) >= 11, names
+    assert len(names) >= 13, names
     raw = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -105,6 +105,8 @@ def test_zero_tokens_is_a_no_op(lib):
 def test_stage_calls_validate(lib):
     v = ctypes.c_void_p(FAKE)
     assert lib.moe_route(v, v, v, 4, 64, 8, 9, v, v, None) == INVALID
+    assert lib.moe_route_ex(v, v, v, 4, 64, 8, 2, v, v, 3, None) == INVALID
+    assert b"router method" in lib.moe_last_error()
     assert lib.moe_route(None, v, v, 4, 64, 8, 2, v, v, None) == INVALID
     assert lib.moe_permute(v, 4, 300, 2, v, v, v, v, None) == INVALID
     assert lib.moe_gate_up(v, v, v, v, v, v, 4, 64, 8, 2, 64, v, 7, None) == INVALID

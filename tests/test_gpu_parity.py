@@ -43,27 +43,32 @@ def _small_inputs(T, E, H, I, k, seed=0, router_bias="normal"):
 # ---------------------------------------------------------------------------
 # router
 # ---------------------------------------------------------------------------
+ROUTE_METHODS = ["exact", "mfma"]
+
+
+@pytest.mark.parametrize("method", ROUTE_METHODS)
 @pytest.mark.parametrize("T,E,H,k", [
     (1, 4, 8, 1), (3, 8, 40, 2), (17, 32, 2880, 4), (65, 128, 2888, 4), (33, 256, 136, 8),
-    (64, 32, 2880, 4), (5, 8, 72, 8), (200, 128, 2880, 4),
+    (64, 32, 2880, 4), (5, 8, 72, 8), (200, 128, 2880, 4), (1000, 48, 2880, 4),
 ])
-def test_route_parity(T, E, H, k):
+def test_route_parity(T, E, H, k, method):
     _need_gpu()
     inp = _small_inputs(T, E, H, 8, k)
-    ids, w = binding.moe_route(dev(inp.x), dev(inp.Wr), dev(inp.br), k)
+    ids, w = binding.moe_route(dev(inp.x), dev(inp.Wr), dev(inp.br), k, method=method)
     torch.cuda.synchronize()
     ids_ref, w_ref, lg = orc.route(inp.x, inp.Wr, inp.br, k)
     assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, lg, k)
 
 
-def test_route_exact_ties_go_to_lower_index():
+@pytest.mark.parametrize("method", ROUTE_METHODS)
+def test_route_exact_ties_go_to_lower_index(method):
     _need_gpu()
     T, E, H, k = 9, 16, 64, 4
     rng = np.random.default_rng(1)
     x = d.f32_to_bf16_bits(rng.normal(0, 1, (T, H)).astype(np.float32))
     Wr = np.repeat(d.f32_to_bf16_bits(rng.normal(0, 0.1, (1, H)).astype(np.float32)), E, 0)
     br = np.zeros(E, np.uint16)
-    ids, w = binding.moe_route(dev(x), dev(Wr), dev(br), k)
+    ids, w = binding.moe_route(dev(x), dev(Wr), dev(br), k, method=method)
     assert (ids.cpu().numpy() == np.arange(k)).all()
     assert np.allclose(w.cpu().numpy(), 1.0 / k, atol=1e-7)
     # structured ties: one-hot router rows pick x's columns; columns 2 and 5 equal
@@ -72,18 +77,45 @@ def test_route_exact_ties_go_to_lower_index():
     x[:, 5] = x[:, 2]
     x[:, 0] = d.f32_to_bf16_bits(np.full(T, -0.0, np.float32))
     x[:, 1] = 0   # +0 ties -0 at index 0
-    ids, _ = binding.moe_route(dev(x), dev(Wr), dev(br), 6)
+    ids, _ = binding.moe_route(dev(x), dev(Wr), dev(br), 6, method=method)
     ids_ref, _, _ = orc.route(x, Wr, br, 6)
     assert (ids.cpu().numpy() == ids_ref).all()
 
 
+@pytest.mark.parametrize("method", ROUTE_METHODS)
+@pytest.mark.parametrize("E,k", [(8, 4), (32, 4), (128, 4), (256, 8)])
+def test_route_near_ties_take_the_exact_decision(E, k, method):
+    """Router rows that differ by a few ulps of one coordinate give logits
+    closer than the float32 accumulation error: the kernel must fall back to
+    the exact logits and decide as the oracle does (float32-rounded exact
+    logits, lower index on equal values)."""
+    _need_gpu()
+    T, H = 97, 2880
+    rng = np.random.default_rng(E)
+    x = d.f32_to_bf16_bits((3.5 * rng.normal(0, 1, (T, H))).astype(np.float32))
+    base = rng.normal(0, 0.02, H).astype(np.float32)
+    W = np.repeat(base[None], E, 0)
+    # a few groups of experts whose rows differ only in coordinate h0 by one
+    # bf16 step; some are exact copies (exact ties)
+    h0 = 7
+    for e in range(E):
+        W[e, h0] = base[h0] * (1.0 + (e % 3) * 2.0 ** -7)
+    Wr = d.f32_to_bf16_bits(W)
+    Wr[E // 2:] = d.f32_to_bf16_bits(rng.normal(0, 0.02, (E - E // 2, H)).astype(np.float32))
+    br = np.zeros(E, np.uint16)
+    ids, w = binding.moe_route(dev(x), dev(Wr), dev(br), k, method=method)
+    ids_ref, w_ref, lg = orc.route(x, Wr, br, k)
+    assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, lg, k)
+
+
+@pytest.mark.parametrize("method", ROUTE_METHODS)
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
-def test_route_configs(name):
+def test_route_configs(name, method):
     _need_gpu()
     cfg = d.CONFIGS[name]
     x = d.make_activations(cfg)
     Wr, br = d.make_router(cfg)
-    ids, w = binding.moe_route(dev(x), dev(Wr), dev(br), cfg.k)
+    ids, w = binding.moe_route(dev(x), dev(Wr), dev(br), cfg.k, method=method)
     ids_ref, w_ref, lg = orc.route(x, Wr, br, cfg.k)
     assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, lg, cfg.k)
 
