@@ -20,10 +20,10 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int E, int k, int32_t* 
 
 // Weight-streaming expert kernels (small token counts per expert).
 hipError_t launch_gemv_gate_up(const void* x, const void* Wgu, const void* bgu, const int32_t* cnt,
-                               const int32_t* off, const int32_t* rows, int H, int E, int k, int I,
-                               void* h, int max_rows_hint, hipStream_t stream);
+                               const int32_t* off, const int32_t* rows, int64_t T, int H, int E, int k, int I,
+                               void* h, hipStream_t stream);
 hipError_t launch_gemv_down(const void* h, const void* Wd, const void* bd, const int32_t* cnt,
-                            const int32_t* off, int H, int E, int I, float* o, int max_rows_hint,
+                            const int32_t* off, int64_t T, int H, int E, int k, int I, float* o,
                             hipStream_t stream);
 
 // LDS-tiled MFMA grouped GEMMs (large token counts per expert).

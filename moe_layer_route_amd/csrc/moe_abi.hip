@@ -95,8 +95,7 @@ int run_gate_up(const char* fn, const void* x, const void* Wgu, const void* bgu,
                 int32_t I, void* h, int32_t path, hipStream_t s) {
   path = choose_path(path, T, E, k);
   if (path == MOE_PATH_GEMV)
-    return hip_status(fn, moe::launch_gemv_gate_up(x, Wgu, bgu, cnt, off, rows, H, E, k, I, h,
-                                                   (int)((T * k + E - 1) / E), s));
+    return hip_status(fn, moe::launch_gemv_gate_up(x, Wgu, bgu, cnt, off, rows, T, H, E, k, I, h, s));
   if (path == MOE_PATH_GEMM)
     return hip_status(fn, moe::launch_gemm_gate_up(x, Wgu, bgu, cnt, off, rows, T, H, E, k, I, h, s));
   return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
@@ -107,8 +106,7 @@ int run_down(const char* fn, const void* h, const void* Wd, const void* bd, cons
              int32_t path, hipStream_t s) {
   path = choose_path(path, T, E, k);
   if (path == MOE_PATH_GEMV)
-    return hip_status(fn, moe::launch_gemv_down(h, Wd, bd, cnt, off, H, E, I, o,
-                                                (int)((T * k + E - 1) / E), s));
+    return hip_status(fn, moe::launch_gemv_down(h, Wd, bd, cnt, off, T, H, E, k, I, o, s));
   if (path == MOE_PATH_GEMM)
     return hip_status(fn, moe::launch_gemm_down(h, Wd, bd, cnt, off, T, H, E, k, I, o, s));
   return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
