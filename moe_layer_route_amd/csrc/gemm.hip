@@ -53,10 +53,6 @@ constexpr int kGmBN = kGmWaves * kGmWN;       // 512
 constexpr int kGmBK = 32;
 constexpr int kGmLdsBufs = 3;
 constexpr int kXcds = 8;
-#ifndef GM_BAND_N
-#define GM_BAND_N 4
-#endif
-constexpr int kGmBandN = GM_BAND_N;   // N tiles per band of the block order
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // a voffset no descriptor here reaches
 
 struct GemmSmem {
@@ -103,15 +99,8 @@ __global__ __launch_bounds__(kGmThreads, 1) void gemm_expert_kernel(
   const int per_xcd = gridDim.x / kXcds;
   const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (L >= n_tiles * m_slots) return;                       // block-uniform
-  // Bands of kGmBandN N tiles: within a band the index runs over the N tiles
-  // of one M-tile slot first, so the workgroups resident on an XCD at once
-  // cover a few M tiles x kGmBandN N tiles and share both their token rows
-  // and their weight slabs through that XCD's L2.
-  const int band = L / (kGmBandN * m_slots);
-  const int band_n = min(kGmBandN, n_tiles - band * kGmBandN);
-  const int idx = L - band * kGmBandN * m_slots;
-  const int ms = idx / band_n;
-  const int nt = band * kGmBandN + (idx - ms * band_n);
+  const int nt = L / m_slots;
+  const int ms = L - nt * m_slots;
 
   // ---- M-tile slot -> (expert, first row) ----
   if (wave == 0) {
