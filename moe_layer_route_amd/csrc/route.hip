@@ -328,10 +328,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 }
 
 // Small batches: one workgroup of 16 waves per token computes every logit
-// exactly (exact products, float64 sum); wave w takes experts w, w+16, ...,
-// four at a time so their row loads overlap.  The token's row of x sits in
-// LDS.  Wave 0 then rounds the logits to float32, takes the top k by
-// (value desc, index asc) and the softmax over the picks in float64.
+// exactly (exact products, float64 sum).  Wave w takes experts w, w+16, ...,
+// two at a time; a unit of work is two experts x up to kExactIters chunks of
+// 8 columns per lane.  Units alternate between two register sets: the loads
+// of unit u+1 are in flight while unit u is multiplied, and the first unit is
+// issued before the token's row of x lands in LDS.  Wave 0 then rounds the
+// logits to float32, takes the top k by (value desc, index asc) and the
+// softmax over the picks in float64.
+constexpr int kExactBatch = 2;    // experts per unit
+constexpr int kExactIters = 4;    // 16-byte chunks per lane and expert per unit
+
 __global__ __launch_bounds__(kRouteThreads) void route_exact_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, const bf16_t* __restrict__ br, int H, int E,
     int k, int32_t* __restrict__ ids, float* __restrict__ wout) {
@@ -342,36 +348,69 @@ __global__ __launch_bounds__(kRouteThreads) void route_exact_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int nchunk = H / 8;
+  const int ngrp = (nchunk + kWave * kExactIters - 1) / (kWave * kExactIters);   // chunk groups per expert
+  const int nbatch = (E - wave + kRouteWaves * kExactBatch - 1) / (kRouteWaves * kExactBatch);
+  const int units = nbatch * ngrp;   // wave-uniform; may be 0 when E < 16
+
+  // unit u = (expert batch u / ngrp, chunk group u % ngrp).  Rows past E and
+  // chunks past H read a valid row / chunk (clamped) that is never used.
+  typedef u32x4_t Set[kExactBatch][kExactIters];
+  auto load = [&](int u, Set& wv) {
+    const int b = u / ngrp, g = u - (u / ngrp) * ngrp;
+#pragma unroll
+    for (int i = 0; i < kExactBatch; ++i) {
+      const int e = min(wave + kRouteWaves * (kExactBatch * b + i), E - 1);
+#pragma unroll
+      for (int it = 0; it < kExactIters; ++it) {
+        const int c = min(lane + kWave * (kExactIters * g + it), nchunk - 1);
+        wv[i][it] = ld16(Wr + (size_t)e * H + 8 * c);
+      }
+    }
+  };
+  // two partial sums per expert (even and odd columns) for a shorter chain
+  double acc[kExactBatch][2];
+#pragma unroll
+  for (int i = 0; i < kExactBatch; ++i) acc[i][0] = acc[i][1] = 0.0;
+  auto compute = [&](int u, const Set& wv) {
+    const int b = u / ngrp, g = u - (u / ngrp) * ngrp;
+#pragma unroll
+    for (int it = 0; it < kExactIters; ++it) {
+      const int c = lane + kWave * (kExactIters * g + it);
+      if (c < nchunk) {
+        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + 8 * c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const double xl = (double)bf16lo(xv[q]), xh = (double)bf16hi(xv[q]);
+#pragma unroll
+          for (int i = 0; i < kExactBatch; ++i) {
+            acc[i][0] = fma(xl, (double)bf16lo(wv[i][it][q]), acc[i][0]);
+            acc[i][1] = fma(xh, (double)bf16hi(wv[i][it][q]), acc[i][1]);
+          }
+        }
+      }
+    }
+    if (g == ngrp - 1) {
+#pragma unroll
+      for (int i = 0; i < kExactBatch; ++i) {
+        const double sum = wave_sum_f64(acc[i][0] + acc[i][1]);
+        const int e = wave + kRouteWaves * (kExactBatch * b + i);
+        if (lane == 0 && e < E) logit[e] = sum + (double)bf16_to_f32(br[e]);
+        acc[i][0] = acc[i][1] = 0.0;
+      }
+    }
+  };
+
+  Set wa, wb;
+  load(0, wa);
   const bf16_t* xrow = x + (size_t)t * H;
   for (int c = threadIdx.x; c < nchunk; c += kRouteThreads)
     *reinterpret_cast<u32x4_t*>(xs + 8 * c) = ld16(xrow + 8 * c);
   __syncthreads();
-  for (int e0 = wave; e0 < E; e0 += 4 * kRouteWaves) {
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int c = lane; c < nchunk; c += kWave) {
-      const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + 8 * c);
-      u32x4_t wv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = min(e0 + kRouteWaves * i, E - 1);
-        wv[i] = ld16(Wr + (size_t)e * H + 8 * c);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const double xl = (double)bf16lo(xv[q]), xh = (double)bf16hi(xv[q]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[i] = fma(xl, (double)bf16lo(wv[i][q]), acc[i]);
-          acc[i] = fma(xh, (double)bf16hi(wv[i][q]), acc[i]);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const double sum = wave_sum_f64(acc[i]);
-      const int e = e0 + kRouteWaves * i;
-      if (lane == 0 && e < E) logit[e] = sum + (double)bf16_to_f32(br[e]);
-    }
+  for (int u = 0; u < units; u += 2) {
+    load(u + 1, wb);   // past the last unit: clamped rows, never used
+    compute(u, wa);
+    load(u + 2, wa);
+    if (u + 1 < units) compute(u + 1, wb);
   }
   __syncthreads();
   if (wave != 0) return;   // no barrier follows
@@ -397,20 +436,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_exact_kernel(
     for (int i = 0; i < kPer; ++i)
       if (lane + kWave * i == e) key[i] = 0;
   }
-  const double l0 = logit[sel[0]];
-  double z[MOE_MAX_K_DEV];
+  // lane j < k takes pick j: one exponential per lane, summed across the
+  // first k lanes in a fixed order (lane 0 + lane 1 + ...)
+  int my = sel[0];
+#pragma unroll
+  for (int j = 1; j < MOE_MAX_K_DEV; ++j)
+    if (lane == j) my = sel[j];
+  const double z = lane < k ? exp(logit[my] - logit[sel[0]]) : 0.0;
   double sum = 0.0;
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_K_DEV; ++j) {
-    z[j] = j < k ? exp(logit[sel[j]] - l0) : 0.0;
-    sum += z[j];
+  for (int j = 0; j < MOE_MAX_K_DEV; ++j) sum += __shfl(z, j, kWave);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = my;
+    wout[(size_t)t * k + lane] = (float)(z / sum);
   }
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_K_DEV; ++j)
-    if (j < k && lane == j) {
-      ids[(size_t)t * k + j] = sel[j];
-      wout[(size_t)t * k + j] = (float)(z[j] / sum);
-    }
 }
 
 }  // namespace
