@@ -15,6 +15,10 @@ Two extra objects:
                 timed with HIP events on the stream it runs on;
   cpu_baseline  the float64 oracle timed on the host cores over a bounded
                 sample of the same workload (a baseline, not the target).
+Context fields: per-step latency percentiles with warm and with cold caches
+(a 512 MiB buffer written before each cold step, outside its events), the
+time per step of a HIP graph replaying one captured step, and what a plain
+1 GiB copy and a bf16 8192^3 hipBLASLt GEMM reach on the same GPU.
 """
 from __future__ import annotations
 
@@ -101,6 +105,54 @@ def cpu_baseline(inp, k, min_seconds=10.0, max_reps=3):
                       f"median of {len(times)} runs of {t:.2f} s"}
 
 
+def _per_step_us(torch, step, stream, n, before=None):
+    """p10 / p50 / p90 of single steps, each between its own pair of events."""
+    import numpy as np
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        if before is not None:
+            before()
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return {"p10": float(np.percentile(us, 10)), "p50": float(np.percentile(us, 50)),
+            "p90": float(np.percentile(us, 90)), "n": n}
+
+
+def _achievable(torch):
+    """What plain library kernels reach on this GPU right now, as context for
+    the roofline fractions (which use the published peaks): a 1 GiB
+    device-to-device copy and a bf16 8192^3 torch.matmul (hipBLASLt)."""
+    import numpy as np
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return float(np.median(ts))
+
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    t_mm = timed(lambda: torch.matmul(a, b))
+    del a, b
+    return {"copy_1GiB_GBs": 2 * (1 << 30) / t_copy / 1e9, "matmul_bf16_8192_TFLOPs": 2 * n ** 3 / t_mm / 1e12}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,9 +201,9 @@ def main(argv=None):
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():
+    def step(st=None):
         binding.moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k=k, y=y, workspace=ws, topk_ids=ids, topk_w=w,
-                            path=args.path, stream=stream)
+                            path=args.path, stream=st if st is not None else stream)
 
     for _ in range(args.warmup):
         step()
@@ -165,6 +217,36 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # Per-step latency: every step between its own pair of events, warm caches.
+    lat = _per_step_us(torch, step, stream, args.steps)
+    # Cold caches: a 512 MiB buffer is written before every step (outside the
+    # events), which evicts the L2s and most of the MALL.
+    flush = torch.empty(1 << 27, dtype=torch.float32, device="cuda")
+    cold = _per_step_us(torch, step, stream, min(args.steps, 20), before=lambda: flush.fill_(1.0))
+    del flush
+    # One step captured in a HIP graph and replayed (the verify-pass setting).
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step(side)
+    stream.wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(torch.cuda.current_stream())
+    graph.replay()
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
+    del graph
+    print(f"[bench] per-step p50 {lat['p50']:.1f} us, cold p50 {cold['p50']:.1f} us, "
+          f"graph replay {graph_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     # Dominant kernel: the same pipeline through the stage calls, with events
     # around every gate_up launch on the stream it is launched on.
@@ -233,6 +315,10 @@ def main(argv=None):
                   "hbm_GBs": layer_bytes / step_s / 1e9, "hbm_frac": layer_bytes / step_s / 1e9 / HBM_PEAK_GBS,
                   "tflops": layer_flops / step_s / 1e12,
                   "mfma_frac": layer_flops / step_s / 1e12 / BF16_PEAK_TFLOPS},
+        "latency_us": lat,
+        "cold_latency_us": cold,
+        "graph_ms_per_step": graph_ms,
+        "achievable": _achievable(torch),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -49,7 +49,7 @@ ROUTE_METHODS = ["exact", "mfma"]
 @pytest.mark.parametrize("method", ROUTE_METHODS)
 @pytest.mark.parametrize("T,E,H,k", [
     (1, 4, 8, 1), (3, 8, 40, 2), (17, 32, 2880, 4), (65, 128, 2888, 4), (33, 256, 136, 8),
-    (64, 32, 2880, 4), (5, 8, 72, 8), (200, 128, 2880, 4), (1000, 48, 2880, 4),
+    (64, 32, 2880, 4), (5, 8, 72, 8), (200, 128, 2880, 4), (1000, 48, 2880, 4), (3, 40, 16384, 4),
 ])
 def test_route_parity(T, E, H, k, method):
     _need_gpu()
@@ -160,6 +160,7 @@ SWEEP = [
     (5, 4, 256, 264, 4),       # k = E
     (257, 8, 136, 128, 2),
     (40, 4, 128, 2888, 1),
+    (3, 4, 16384, 40, 2),      # largest H: many K steps / chunk groups
 ]
 
 
