@@ -126,7 +126,7 @@ def test_route_configs(name, method):
 @pytest.mark.parametrize("T,E,k,skew", [
     (1, 4, 1, "uniform"), (7, 8, 4, "uniform"), (64, 32, 4, "uniform"), (257, 128, 4, "uniform"),
     (4096, 32, 4, "uniform"), (16384, 128, 4, "zipf"), (1000, 256, 8, "uniform"), (300, 16, 2, "one"),
-    (5000, 3, 1, "uniform"),
+    (5000, 3, 1, "uniform"), (4097, 64, 4, "uniform"), (8193, 8, 2, "one"), (20480, 256, 8, "zipf"),
 ])
 def test_permute_parity(T, E, k, skew):
     _need_gpu()
