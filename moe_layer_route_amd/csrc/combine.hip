@@ -13,6 +13,9 @@ namespace {
 
 constexpr int kCombineThreads = 256;
 
+// KMAX >= k slots per token; every load of a thread is issued before the
+// first product (slots past k re-read slot 0 and are left out of the sum).
+template <int KMAX>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float* __restrict__ o, const int32_t* __restrict__ pos, const float* __restrict__ w,
     int64_t T, int H, int k, bf16_t* __restrict__ y) {
@@ -22,15 +25,27 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   if (item >= T * quads) return;   // no barrier in this kernel
   const int64_t t = item / quads;
   const int n = 4 * (int)(item - t * quads);
+  int p[KMAX];
+  float wj[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const size_t s = (size_t)t * k + (j < k ? j : 0);
+    p[j] = pos[s];
+    wj[j] = w[s];
+  }
+  f32x4_t v[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)   // read once: non-temporal
+    v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(o + (size_t)p[j] * H + n));
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const size_t s = (size_t)t * k + j;
-    const float wj = w[s];
-    const float4 v = *reinterpret_cast<const float4*>(o + (size_t)pos[s] * H + n);
-    a0 = fmaf(wj, v.x, a0);
-    a1 = fmaf(wj, v.y, a1);
-    a2 = fmaf(wj, v.z, a2);
-    a3 = fmaf(wj, v.w, a3);
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      a0 = fmaf(wj[j], v[j][0], a0);
+      a1 = fmaf(wj[j], v[j][1], a1);
+      a2 = fmaf(wj[j], v[j][2], a2);
+      a3 = fmaf(wj[j], v[j][3], a3);
+    }
   }
   u32x2_t out = {pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
   *reinterpret_cast<u32x2_t*>(y + (size_t)t * H + n) = out;
@@ -42,8 +57,8 @@ hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, in
                           void* y, hipStream_t stream) {
   const int64_t items = T * (H / 4);
   dim3 grid((unsigned)((items + kCombineThreads - 1) / kCombineThreads));
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, stream, o, pos, w, T, H, k,
-                     (bf16_t*)y);
+  auto kern = k <= 4 ? combine_kernel<4> : combine_kernel<MOE_MAX_K_DEV>;
+  hipLaunchKernelGGL(kern, grid, dim3(kCombineThreads), 0, stream, o, pos, w, T, H, k, (bf16_t*)y);
   return hipGetLastError();
 }
 
