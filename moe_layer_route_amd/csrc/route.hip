@@ -88,19 +88,34 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 }
 
 // Exact-product, float64-sum logit of one (token, expert) pair by one wave.
+// Each lane's chunks (8 columns, every 64th) are loaded ITERS at a time, all
+// before the first product, so a row of up to 512 ITERS columns costs one
+// memory round trip.
+template <int ITERS>
 __device__ double logit_f64(const bf16_t* __restrict__ xrow, const bf16_t* __restrict__ wrow, double bias,
                             int H, int lane) {
-  double acc = 0.0;
-  for (int c = lane; c < H / 8; c += kWave) {
-    const u32x4_t xv = ld16(xrow + 8 * c);
-    const u32x4_t wv = ld16(wrow + 8 * c);
+  const int nchunk = H / 8;
+  double a0 = 0.0, a1 = 0.0;
+  for (int c0 = 0; c0 < nchunk; c0 += kWave * ITERS) {
+    u32x4_t xv[ITERS], wv[ITERS];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc = fma((double)bf16lo(xv[q]), (double)bf16lo(wv[q]), acc);
-      acc = fma((double)bf16hi(xv[q]), (double)bf16hi(wv[q]), acc);
+    for (int it = 0; it < ITERS; ++it) {
+      const int c = min(c0 + lane + kWave * it, nchunk - 1);   // clamped; the tail is left out below
+      xv[it] = ld16(xrow + 8 * c);
+      wv[it] = ld16(wrow + 8 * c);
+    }
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      if (c0 + lane + kWave * it < nchunk) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          a0 = fma((double)bf16lo(xv[it][q]), (double)bf16lo(wv[it][q]), a0);
+          a1 = fma((double)bf16hi(xv[it][q]), (double)bf16hi(wv[it][q]), a1);
+        }
+      }
     }
   }
-  return wave_sum_f64(acc) + bias;
+  return wave_sum_f64(a0 + a1) + bias;
 }
 
 // TG = 16-token groups per workgroup (each B fragment feeds TG MFMAs).
@@ -284,7 +299,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
           const int src = __ffsll((unsigned long long)m) - 1;
           m &= m - 1;
           const int ec = src + kWave * i;
-          const double l64 = logit_f64(xrow, Wr + (size_t)ec * H, (double)bf16_to_f32(br[ec]), H, lane);
+          // (fewer loads in flight for the 64-token variant: its registers are full)
+          const double l64 =
+              logit_f64<TG == 1 ? 8 : 4>(xrow, Wr + (size_t)ec * H, (double)bf16_to_f32(br[ec]), H, lane);
           if (lane == src) {
             lx[i] = l64;
             key2[i] = make_key((float)l64, ec);
