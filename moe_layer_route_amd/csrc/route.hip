@@ -134,81 +134,174 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   const int g = lane >> 4;
   const int c = lane & 15;
 
-  // ---- phase 1: this wave's 16 experts x 16 tokens over its slice of K
-  const int grp = wave % groups_p2;              // 16-expert group
-  const int ks = wave / groups_p2;               // K slice
-  const int nslices = kRouteWaves / groups_p2;
   const int nk = (H + 31) / 32;
-  const int kb_begin = (nk * ks) / nslices;
-  const int kb_end = (nk * (ks + 1)) / nslices;
   const rsrc_t x_rs = make_rsrc(x, (uint32_t)((size_t)T * H * 2));
   const rsrc_t w_rs = make_rsrc(Wr, (uint32_t)((size_t)E * H * 2));
-  const uint32_t a_off = ((uint32_t)(t0 + c) * H + 8u * g) * 2u;   // + 16 H * 2 per token group
-  const uint32_t b_off = ((uint32_t)(16 * grp + c) * H + 8u * g) * 2u;
-  const bool active = 16 * grp < E;              // wave-uniform
-
-  f32x4_t acc[TG], aab[TG];
-#pragma unroll
-  for (int i = 0; i < TG; ++i) {
-    acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    aab[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  if (active) {
-    // Loads run kRouteDepth steps ahead in a ring of registers.  All loads are
-    // unconditional: rows past T or E read as 0 (outside the descriptors), and
-    // K steps outside this wave's slice or past H are sent outside on purpose.
-    // (The scalar offset operand must be wave-uniform, so the per-lane tests
-    // go into the vector offset.)
-    struct Ld { u32x4_t a[TG]; u32x4_t b; };
-    Ld ring[kRouteDepth];
-    auto load = [&](int kb, Ld& d) {
-      const bool k_ok = kb < kb_end && kb * 32 + 8 * g < H;
-      const uint32_t koff = 64u * kb;
-#pragma unroll
-      for (int i = 0; i < TG; ++i)
-        d.a[i] = buf_ld16(x_rs, k_ok ? a_off + koff + (uint32_t)(32 * i) * H : 0xFFFFFFF0u, 0);
-      d.b = buf_ld16(w_rs, k_ok ? b_off + koff : 0xFFFFFFF0u, 0);
+  // float32 additions in sequence on the way to a logit (K steps of one
+  // accumulator, the slice sums, the in-MFMA sums and the bias), never
+  // counted below the 128 the error analysis was made for
+  float err_steps;
+  if constexpr (TG == 4) {
+    // ---- phase 1, 64 tokens x up to 128 experts: each K step's x tile
+    // (4 x 16 token rows) and router tile (8 x 16 expert rows) are loaded
+    // once into fragment-major LDS (double buffered, inside s_logit) and wave
+    // w multiplies token group w%4 with expert groups 2(w/4) and 2(w/4)+1 over
+    // all of K.  Waves 0-11 each copy one 16-byte piece per K step (waves 0-3
+    // x, 4-11 the router), two steps ahead.
+    static_assert(EMAX == 128, "64-token router tile holds 128 experts");
+    constexpr int kFr = 12;                                    // fragments per K step
+    u32x4_t* stage = reinterpret_cast<u32x4_t*>(&s_logit[0][0]);   // [2][kFr][64], 24 KB
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const bool loader = wv < kFr;
+    // waves 12-15 load wave 0's piece too and never store it: every load is
+    // unconditional (a load under a branch makes the compiler wait for all
+    // loads at the merge)
+    const bool ld_x = wv < 4 || !loader;
+    const rsrc_t ld_rs = ld_x ? x_rs : w_rs;
+    const int ld_row = wv < 4 ? t0 + 16 * wv + c : loader ? 16 * (wv - 4) + c : t0 + c;
+    const uint32_t ld_off = ((uint32_t)ld_row * H + 8u * g) * 2u;
+    auto gload = [&](int kb, u32x4_t& r) {
+      const bool k_ok = kb * 32 + 8 * g < H;
+      r = buf_ld16(ld_rs, k_ok ? ld_off + 64u * kb : 0xFFFFFFF0u, 0);
     };
-#pragma unroll
-    for (int d = 0; d < kRouteDepth; ++d) load(kb_begin + d, ring[d]);
-    for (int kb0 = kb_begin; kb0 < kb_end; kb0 += kRouteDepth) {
-#pragma unroll
-      for (int d = 0; d < kRouteDepth; ++d) {
-        const u32x4_t bb = abs_bf16x8(ring[d].b);
-#pragma unroll
-        for (int i = 0; i < TG; ++i) {
-          acc[i] = mfma16x16x32(ring[d].a[i], ring[d].b, acc[i]);
-          aab[i] = mfma16x16x32(abs_bf16x8(ring[d].a[i]), bb, aab[i]);
-        }
-        load(kb0 + d + kRouteDepth, ring[d]);
+    auto lstore = [&](int buf, const u32x4_t& r) { stage[(buf * kFr + wv) * kWave + lane] = r; };
+    const int ti = wave & 3, gp = wave >> 2;
+    const bool act0 = 32 * gp < E, act1 = 32 * gp + 16 < E;   // wave-uniform
+    f32x4_t acc2[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    f32x4_t aab2[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    auto compute = [&](int buf) {
+      const u32x4_t* st = stage + buf * kFr * kWave + lane;
+      const u32x4_t a = st[ti * kWave];
+      const u32x4_t aa = abs_bf16x8(a);
+      if (act0) {
+        const u32x4_t b = st[(4 + 2 * gp) * kWave];
+        acc2[0] = mfma16x16x32(a, b, acc2[0]);
+        aab2[0] = mfma16x16x32(aa, abs_bf16x8(b), aab2[0]);
       }
+      if (act1) {
+        const u32x4_t b = st[(5 + 2 * gp) * kWave];
+        acc2[1] = mfma16x16x32(a, b, acc2[1]);
+        aab2[1] = mfma16x16x32(aa, abs_bf16x8(b), aab2[1]);
+      }
+    };
+    // Step kb: load kb+2, multiply kb (buffer kb%2), store kb+1 (loaded one
+    // step ago) into the other buffer, barrier.  The other buffer was last
+    // read during step kb-1, before the previous barrier.  The step count is
+    // rounded up to even: a step past the end reads zeros and adds 0.
+    u32x4_t R0, R1;
+    gload(0, R0);
+    gload(1, R1);
+    if (loader) lstore(0, R0);
+    __syncthreads();
+    const int nk2 = (nk + 1) / 2 * 2;
+    for (int kb = 0; kb < nk2; kb += 2) {
+      gload(kb + 2, R0);
+      compute(0);
+      if (loader) lstore(1, R1);
+      __syncthreads();
+      gload(kb + 3, R1);
+      compute(1);
+      if (loader) lstore(0, R0);
+      __syncthreads();
     }
-  }
-  // sum the K slices in slice order (16x16 accumulator layout: lane l,
-  // element v = token 4*(l/16)+v, expert 16*grp + l%16)
-  const int e_mine = 16 * grp + c;
-  for (int s = 0; s < nslices; ++s) {
-    if (s == ks && active && e_mine < E) {
+    // 16x16 accumulator layout: lane l, element v = token 16 ti + 4 (l/16) + v,
+    // expert 16 (2 gp + q) + l%16.  The staging buffers are dead after the
+    // last barrier above.
 #pragma unroll
-      for (int i = 0; i < TG; ++i)
+    for (int q = 0; q < 2; ++q) {
+      const int e = 16 * (2 * gp + q) + c;
+      if (e < E)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int tt = 16 * i + 4 * g + v;
-          if (s == 0) {
-            s_logit[tt][e_mine] = acc[i][v];
-            s_abs[tt][e_mine] = aab[i][v];
-          } else {
-            s_logit[tt][e_mine] += acc[i][v];
-            s_abs[tt][e_mine] += aab[i][v];
-          }
+          const int tt = 16 * ti + 4 * g + v;
+          s_logit[tt][e] = acc2[q][v];
+          s_abs[tt][e] = aab2[q][v];
         }
     }
     __syncthreads();
+    err_steps = fmaxf(128.f, (float)(nk2 + 40));
+  } else {
+    // ---- phase 1: this wave's 16 experts x 16 tokens over its slice of K
+    const int grp = wave % groups_p2;              // 16-expert group
+    const int ks = wave / groups_p2;               // K slice
+    const int nslices = kRouteWaves / groups_p2;
+    const int kb_begin = (nk * ks) / nslices;
+    const int kb_end = (nk * (ks + 1)) / nslices;
+    const uint32_t a_off = ((uint32_t)(t0 + c) * H + 8u * g) * 2u;   // + 16 H * 2 per token group
+    const uint32_t b_off = ((uint32_t)(16 * grp + c) * H + 8u * g) * 2u;
+    const bool active = 16 * grp < E;              // wave-uniform
+
+    f32x4_t acc[TG], aab[TG];
+#pragma unroll
+    for (int i = 0; i < TG; ++i) {
+      acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      aab[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    if (active) {
+      // Loads run kRouteDepth steps ahead in a ring of registers.  All loads are
+      // unconditional: rows past T or E read as 0 (outside the descriptors), and
+      // K steps outside this wave's slice or past H are sent outside on purpose.
+      // (The scalar offset operand must be wave-uniform, so the per-lane tests
+      // go into the vector offset.)
+      struct Ld { u32x4_t a[TG]; u32x4_t b; };
+      Ld ring[kRouteDepth];
+      auto load = [&](int kb, Ld& d) {
+        const bool k_ok = kb < kb_end && kb * 32 + 8 * g < H;
+        const uint32_t koff = 64u * kb;
+#pragma unroll
+        for (int i = 0; i < TG; ++i)
+          d.a[i] = buf_ld16(x_rs, k_ok ? a_off + koff + (uint32_t)(32 * i) * H : 0xFFFFFFF0u, 0);
+        d.b = buf_ld16(w_rs, k_ok ? b_off + koff : 0xFFFFFFF0u, 0);
+      };
+#pragma unroll
+      for (int d = 0; d < kRouteDepth; ++d) load(kb_begin + d, ring[d]);
+      for (int kb0 = kb_begin; kb0 < kb_end; kb0 += kRouteDepth) {
+#pragma unroll
+        for (int d = 0; d < kRouteDepth; ++d) {
+          const u32x4_t bb = abs_bf16x8(ring[d].b);
+#pragma unroll
+          for (int i = 0; i < TG; ++i) {
+            acc[i] = mfma16x16x32(ring[d].a[i], ring[d].b, acc[i]);
+            aab[i] = mfma16x16x32(abs_bf16x8(ring[d].a[i]), bb, aab[i]);
+          }
+          load(kb0 + d + kRouteDepth, ring[d]);
+        }
+      }
+    }
+    // sum the K slices in slice order (16x16 accumulator layout: lane l,
+    // element v = token 4*(l/16)+v, expert 16*grp + l%16)
+    const int e_mine = 16 * grp + c;
+    for (int s = 0; s < nslices; ++s) {
+      if (s == ks && active && e_mine < E) {
+#pragma unroll
+        for (int i = 0; i < TG; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int tt = 16 * i + 4 * g + v;
+            if (s == 0) {
+              s_logit[tt][e_mine] = acc[i][v];
+              s_abs[tt][e_mine] = aab[i][v];
+            } else {
+              s_logit[tt][e_mine] += acc[i][v];
+              s_abs[tt][e_mine] += aab[i][v];
+            }
+          }
+      }
+      __syncthreads();
+    }
+
+    err_steps = fmaxf(128.f, (float)((nk + nslices - 1) / nslices + nslices + 40));
   }
 
   // ---- phase 2: one wave per token, waves take every 16th token ----
-  constexpr int kPer = MOE_MAX_E_DEV / kWave;   // experts per lane
+  constexpr int kPer = EMAX / kWave;             // experts per lane
   constexpr float u = 5.9604645e-8f;             // 2^-24
+  float bias[kPer];                              // this lane's router biases, for every token
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + kWave * i;
+    bias[i] = e < E ? bf16_to_f32(br[e]) : 0.f;
+  }
   for (int tt = wave; tt < kRouteTok; tt += kRouteWaves) {
     const int t = t0 + tt;
     if (t >= T) break;                                       // wave-uniform, no barrier follows
@@ -221,10 +314,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       lv[i] = -INFINITY;
       dv[i] = 0.f;
       if (e < E) {
-        const float l = s_logit[tt][e] + bf16_to_f32(br[e]);
+        const float l = s_logit[tt][e] + bias[i];
         lv[i] = l;
         // error bound of the float32 logit, doubled, plus two ulps of it
-        dv[i] = 2.f * (128.f * u * s_abs[tt][e] + 2.f * u * fabsf(l)) + 2.4e-7f * fabsf(l) + 1e-30f;
+        dv[i] = 2.f * (err_steps * u * s_abs[tt][e] + 2.f * u * fabsf(l)) + 2.4e-7f * fabsf(l) + 1e-30f;
         key[i] = make_key(l, e);
       }
     }
@@ -327,20 +420,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         wl[j] = __shfl(l, e % kWave, kWave);
       }
     }
-    // lane j writes pick j
-    double z[MOE_MAX_K_DEV];
+    // lane j < k takes pick j: one exponential per lane, summed across the
+    // first k lanes in a fixed order (lane 0 + lane 1 + ...)
+    int my = sel[0];
+    double myl = wl[0];
+#pragma unroll
+    for (int j = 1; j < MOE_MAX_K_DEV; ++j)
+      if (lane == j) {
+        my = sel[j];
+        myl = wl[j];
+      }
+    const double z = lane < k ? exp(myl - wl[0]) : 0.0;
     double sum = 0.0;
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_K_DEV; ++j) {
-      z[j] = j < k ? exp(wl[j] - wl[0]) : 0.0;
-      sum += z[j];
+    for (int j = 0; j < MOE_MAX_K_DEV; ++j) sum += __shfl(z, j, kWave);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = my;
+      wout[(size_t)t * k + lane] = (float)(z / sum);
     }
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_K_DEV; ++j)
-      if (j < k && lane == j) {
-        ids[(size_t)t * k + j] = sel[j];
-        wout[(size_t)t * k + j] = (float)(z[j] / sum);
-      }
   }
 }
 

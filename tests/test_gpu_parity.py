@@ -50,6 +50,7 @@ ROUTE_METHODS = ["exact", "mfma"]
 @pytest.mark.parametrize("T,E,H,k", [
     (1, 4, 8, 1), (3, 8, 40, 2), (17, 32, 2880, 4), (65, 128, 2888, 4), (33, 256, 136, 8),
     (64, 32, 2880, 4), (5, 8, 72, 8), (200, 128, 2880, 4), (1000, 48, 2880, 4), (3, 40, 16384, 4),
+    (8195, 40, 136, 4), (8256, 128, 2888, 4),   # 64-token tiles: token, expert and K tails
 ])
 def test_route_parity(T, E, H, k, method):
     _need_gpu()
