@@ -159,6 +159,35 @@ MOE_API int moe_forward_ex(const void* x, const void* Wr, const void* br,
                    void* workspace, size_t workspace_bytes, int32_t path, void* stream);
 
 /*
+ * moe_forward_ep -- one expert-parallel rank's share of the layer: experts
+ * are split across ranks by contiguous ranges, every rank routes all T tokens
+ * over all E experts, keeps only the (token, slot) pairs whose expert it holds
+ * (the others are skipped, never multiplied by 0) and returns its part of y.
+ * Summing y_partial over the ranks gives y (xserv "Phase 19: gpt-oss-20b MoE
+ * support", section 2: expert parallelism filters by expert range and the
+ * partial outputs are summed by one all-reduce).
+ *
+ *   x, Wr, br            as in moe_forward (the whole router: [E][H], [E])
+ *   e_begin, n_local     this rank holds experts [e_begin, e_begin + n_local)
+ *   Wgu_local bf16 [n_local][H][2I], bgu_local bf16 [n_local][2I],
+ *   Wd_local bf16 [n_local][I][H], bd_local bf16 [n_local][H]: those experts
+ *   y_partial float [T][H] out: sum over this rank's experts of
+ *                        topk_w[t][j] * (h_j . Wd[e_j] + bd[e_j]), in float32
+ *                        (0 for a token none of whose experts is here)
+ *   topk_ids_out, topk_w_out, workspace, workspace_bytes, path: as in
+ *                        moe_forward_ex; the workspace size is
+ *                        moe_workspace_bytes(T, H, E, k, I) with the full E.
+ * Errors: the range must satisfy 0 <= e_begin, 1 <= n_local,
+ * e_begin + n_local <= E (MOE_ERR_INVALID_ARG otherwise); other checks as in
+ * moe_forward.
+ */
+MOE_API int moe_forward_ep(const void* x, const void* Wr, const void* br,
+                   const void* Wgu_local, const void* bgu_local, const void* Wd_local, const void* bd_local,
+                   int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, int32_t e_begin, int32_t n_local,
+                   float* y_partial, int32_t* topk_ids_out, float* topk_w_out,
+                   void* workspace, size_t workspace_bytes, int32_t path, void* stream);
+
+/*
  * moe_permute -- expert-contiguous order of the T*k (token, slot) pairs: the
  * device-side bookkeeping that replaces copying every token to every expert
  * (forward pipeline; ids never leave the device).
@@ -169,7 +198,8 @@ MOE_API int moe_forward_ex(const void* x, const void* Wr, const void* br,
  *   rows int32 [T*k]  out: rows[off[e] + r] = the r-th slot s = t*k + j with
  *                     topk_ids[t][j] == e, in increasing s (stable)
  *   pos  int32 [T*k]  out: inverse of rows (rows[pos[s]] == s)
- * Every id must lie in [0, E); other values are undefined behaviour.
+ * A slot whose id lies outside [0, E) is skipped: it appears in no segment of
+ * rows, pos[s] = -1, and off[E] counts only the others.
  */
 MOE_API int moe_permute(const int32_t* topk_ids, int64_t T, int32_t E, int32_t k,
                 int32_t* cnt, int32_t* off, int32_t* rows, int32_t* pos, void* stream);
@@ -208,7 +238,8 @@ MOE_API int moe_down(const void* h, const void* Wd, const void* bd,
  *
  *   o float [T*k][H] (moe_down), pos int32 [T*k] (moe_permute),
  *   topk_w float [T][k] (moe_route)
- *   y bf16 [T][H] out: y[t] = sum_j topk_w[t][j] * o[pos[t*k + j]]
+ *   y bf16 [T][H] out: y[t] = sum_j topk_w[t][j] * o[pos[t*k + j]], over the
+ *                     slots with pos >= 0 (skipped slots add nothing)
  */
 MOE_API int moe_combine(const float* o, const int32_t* pos, const float* topk_w,
                 int64_t T, int32_t H, int32_t k, void* y, void* stream);

@@ -24,7 +24,8 @@ LIB_PATH = os.environ.get("MOE_LAYER_ROUTE_LIB") or os.path.join(
 
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace_bytes", "moe_expert_path",
            "moe_route", "moe_route_ex",
-           "moe_forward", "moe_forward_ex", "moe_permute", "moe_gate_up", "moe_down", "moe_combine")
+           "moe_forward", "moe_forward_ex", "moe_forward_ep", "moe_permute", "moe_gate_up", "moe_down",
+           "moe_combine")
 
 
 class MoEError(RuntimeError):
@@ -44,6 +45,8 @@ _SIGS = {
     "moe_route_ex": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _i32, _vp]),
     "moe_forward": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _vp]),
     "moe_forward_ex": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _i32, _vp]),
+    "moe_forward_ep": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 4
+                       + [_sz, _i32, _vp]),
     "moe_permute": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "moe_gate_up": (ctypes.c_int, [_vp] * 6 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
     "moe_down": (ctypes.c_int, [_vp] * 5 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
@@ -165,6 +168,30 @@ def moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k: int = 4, y=None, workspace=None,
 
 def moe_forward_ex(*args, **kw):
     return moe_forward(*args, **kw)
+
+
+def moe_forward_ep(x, Wr, br, Wgu_local, bgu_local, Wd_local, bd_local, e_begin: int, k: int = 4,
+                   y_partial=None, workspace=None, topk_ids=None, topk_w=None, path="auto", stream=None):
+    """One expert-parallel rank's share: experts [e_begin, e_begin + n_local) of the E
+    routed ones (n_local = Wgu_local.shape[0]); returns y_partial (float32 [T,H])."""
+    _dev(x, Wr, br, Wgu_local, bgu_local, Wd_local, bd_local)
+    _b16(x, Wr, br, Wgu_local, bgu_local, Wd_local, bd_local)
+    T, H = x.shape
+    E = Wr.shape[0]
+    n_local = Wgu_local.shape[0]
+    I = Wd_local.shape[1]
+    if y_partial is None:
+        y_partial = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(T, H, E, k, I, x.device)
+    _dev(y_partial, workspace, topk_ids, topk_w)
+    st = library().moe_forward_ep(_ptr(x), _ptr(Wr), _ptr(br), _ptr(Wgu_local), _ptr(bgu_local),
+                                  _ptr(Wd_local), _ptr(bd_local), T, H, E, k, I, e_begin, n_local,
+                                  _ptr(y_partial), _ptr(topk_ids), _ptr(topk_w), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), path_code(path),
+                                  _stream(stream))
+    _check(st, "moe_forward_ep")
+    return y_partial
 
 
 def moe_permute(topk_ids, E: int, stream=None):

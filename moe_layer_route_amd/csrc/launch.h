@@ -15,8 +15,10 @@ namespace moe {
 hipError_t launch_route(const void* x, const void* Wr, const void* br, int64_t T, int H, int E, int k,
                         int32_t* ids, float* w, int method, hipStream_t stream);
 
+// e_begin: expert ids are counted from it; slots whose expert is outside
+// [e_begin, e_begin + E) are skipped (pos = -1)
 hipError_t launch_permute(const int32_t* ids, int64_t T, int E, int k, int32_t* cnt, int32_t* off,
-                          int32_t* rows, int32_t* pos, hipStream_t stream);
+                          int32_t* rows, int32_t* pos, hipStream_t stream, int e_begin = 0);
 
 // Weight-streaming expert kernels (small token counts per expert).
 hipError_t launch_gemv_gate_up(const void* x, const void* Wgu, const void* bgu, const int32_t* cnt,
@@ -34,7 +36,8 @@ hipError_t launch_gemm_down(const void* h, const void* Wd, const void* bd, const
                             const int32_t* off, int64_t T, int H, int E, int k, int I, float* o,
                             hipStream_t stream);
 
+// slots with pos < 0 are left out; out_f32: y is float32 (partial sums), else bf16
 hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, int64_t T, int H, int k,
-                          void* y, hipStream_t stream);
+                          void* y, hipStream_t stream, bool out_f32 = false);
 
 }  // namespace moe

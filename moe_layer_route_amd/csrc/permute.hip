@@ -25,8 +25,10 @@
 // popcount of the lower lanes, and the lowest lane of the group advances the
 // wave's base for that expert.  The result is the stable order (by slot
 // index) and is identical on every run, whatever the number of chunks.
-// An id outside [0, E) (undefined input) is skipped, so every access stays in
-// bounds.
+// Experts are counted from e_begin: slot s goes to local expert
+// ids[s] - e_begin, and a slot whose local expert is outside [0, E) is
+// skipped and gets pos = -1 (an expert-parallel rank keeps only the experts
+// it holds; with e_begin = 0 and every id in [0, E) nothing is skipped).
 #include "device_common.h"
 #include "launch.h"
 
@@ -48,7 +50,8 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 }
 
 __global__ __launch_bounds__(kPermHistThreads) void permute_hist_kernel(const int32_t* __restrict__ ids, int S,
-                                                                         int E, int32_t* __restrict__ hist) {
+                                                                         int e_begin, int E,
+                                                                         int32_t* __restrict__ hist) {
   __shared__ int h[MOE_MAX_E_DEV];
   for (int e = threadIdx.x; e < MOE_MAX_E_DEV; e += kPermHistThreads) h[e] = 0;
   __syncthreads();
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(kPermHistThreads) void permute_hist_kernel(const in
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int s = s_begin + threadIdx.x + kPermHistThreads * i;
-    e[i] = s < s_end ? ids[s] : -1;
+    e[i] = s < s_end ? ids[s] - e_begin : -1;
   }
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(kPermHistThreads) void permute_hist_kernel(const in
 // hist: the per-chunk counts (nchunks > 1), or null for a single chunk, which
 // then also writes pos.
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
-    const int32_t* __restrict__ ids, int S, int E, const int32_t* __restrict__ hist, int nchunks,
+    const int32_t* __restrict__ ids, int S, int e_begin, int E, const int32_t* __restrict__ hist, int nchunks,
     int32_t* __restrict__ cnt, int32_t* __restrict__ off, int32_t* __restrict__ rows, int32_t* __restrict__ pos) {
   __shared__ int whist[kPermWaves][MOE_MAX_E_DEV];
   __shared__ int base[MOE_MAX_E_DEV];
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   const int s_end = c_begin + min(c_len, wave * per + per);
 
   for (int s = s_begin + lane; s < s_end; s += kWave) {
-    const int e = ids[s];
+    const int e = ids[s] - e_begin;
     if ((unsigned)e < (unsigned)E) atomicAdd(&whist[wave][e], 1);
   }
   __syncthreads();
@@ -157,8 +160,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
   for (int sb = s_begin; sb < s_end; sb += kWave) {
     const int s = sb + lane;
-    const int id = s < s_end ? ids[s] : -1;
-    const bool valid = (unsigned)id < (unsigned)E;   // ids outside [0, E) are skipped
+    const int id = s < s_end ? ids[s] - e_begin : -1;
+    const bool valid = (unsigned)id < (unsigned)E;   // slots outside [0, E) are skipped
     const int e = valid ? id : 0;
     uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -178,38 +181,43 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
       const int p = wbase + __popcll(peers & lt_mask);
       rows[p] = s;
       if (write_pos) pos[s] = p;
+    } else if (write_pos && s < s_end) {
+      pos[s] = -1;
     }
   }
 }
 
-// rows[0 .. off[E]) are the written entries (all S of them unless some id was
-// outside [0, E)).
-__global__ __launch_bounds__(256) void permute_inverse_kernel(const int32_t* __restrict__ rows,
+// rows[0 .. off[E]) are the written entries; every other slot is a skipped
+// one.  The two kinds of writes go to different slots.
+__global__ __launch_bounds__(256) void permute_inverse_kernel(const int32_t* __restrict__ ids, int S, int e_begin,
+                                                              const int32_t* __restrict__ rows,
                                                               const int32_t* __restrict__ off, int E,
                                                               int32_t* __restrict__ pos) {
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p < off[E]) pos[rows[p]] = p;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < S && (unsigned)(ids[i] - e_begin) >= (unsigned)E) pos[i] = -1;
+  if (i < off[E]) pos[rows[i]] = i;
 }
 
 }  // namespace
 
 hipError_t launch_permute(const int32_t* ids, int64_t T, int E, int k, int32_t* cnt, int32_t* off,
-                          int32_t* rows, int32_t* pos, hipStream_t stream) {
+                          int32_t* rows, int32_t* pos, hipStream_t stream, int e_begin) {
   const int S = (int)(T * k);
   // one chunk up to kMultiMin slots; above, the per-chunk counts (nchunks x E
   // <= S/16 + 256 <= S entries) fit in pos
   constexpr int kMultiMin = 4 * kPermChunk;
   if (S < kMultiMin) {
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, ids, S, E, (const int32_t*)nullptr,
-                       1, cnt, off, rows, pos);
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, ids, S, e_begin, E,
+                       (const int32_t*)nullptr, 1, cnt, off, rows, pos);
     return hipGetLastError();
   }
   const int nchunks = (S + kPermChunk - 1) / kPermChunk;
-  hipLaunchKernelGGL(permute_hist_kernel, dim3(nchunks), dim3(kPermHistThreads), 0, stream, ids, S, E, pos);
-  hipLaunchKernelGGL(permute_kernel, dim3(nchunks), dim3(kPermThreads), 0, stream, ids, S, E,
+  hipLaunchKernelGGL(permute_hist_kernel, dim3(nchunks), dim3(kPermHistThreads), 0, stream, ids, S, e_begin, E,
+                     pos);
+  hipLaunchKernelGGL(permute_kernel, dim3(nchunks), dim3(kPermThreads), 0, stream, ids, S, e_begin, E,
                      (const int32_t*)pos, nchunks, cnt, off, rows, (int32_t*)nullptr);
-  hipLaunchKernelGGL(permute_inverse_kernel, dim3((S + 255) / 256), dim3(256), 0, stream, (const int32_t*)rows,
-                     (const int32_t*)off, E, pos);
+  hipLaunchKernelGGL(permute_inverse_kernel, dim3((S + 255) / 256), dim3(256), 0, stream, ids, S, e_begin,
+                     (const int32_t*)rows, (const int32_t*)off, E, pos);
   return hipGetLastError();
 }
 

@@ -143,12 +143,16 @@ def expert_permutation(ids: np.ndarray, E: int):
 # --------------------------------------------------------------------------
 # Whole block, sparse formulation: only selected experts are read
 # --------------------------------------------------------------------------
-def moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k: int, tokens=None, keep=False):
+def moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k: int, tokens=None, keep=False, experts=None):
     """Full forward.  Returns a dict with y [T', H] float64, ids, w, logits,
     and, if keep, u/h/o per slot [T'*k, ...] in slot order s = t*k + j.
 
     tokens: optional array of token indices; the result then covers only those
-    rows of x (used to check sampled outputs at full size)."""
+    rows of x (used to check sampled outputs at full size).
+    experts: optional (e_begin, e_end): y then sums only the slots whose expert
+    lies in that range -- one expert-parallel rank's share (section 2 of the
+    Phase 19 page: expert parallelism filters by expert range and sums the
+    ranks' partial outputs).  The weights stay indexed by global expert id."""
     ids, w, lg = route(x if tokens is None else x[np.asarray(tokens)], Wr, br, k)
     xs = widen(x if tokens is None else x[np.asarray(tokens)])
     T, H = xs.shape
@@ -160,7 +164,8 @@ def moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k: int, tokens=None, keep=False):
         h_all = np.zeros((T * k, I2 // 2))
         o_all = np.zeros((T * k, Wd.shape[2]))
     flat = ids.reshape(-1)
-    for e in range(E):
+    e_lo, e_hi = (0, E) if experts is None else experts
+    for e in range(e_lo, e_hi):
         slots = np.nonzero(flat == e)[0]
         if slots.size == 0:
             continue               # skipped, never multiplied by zero

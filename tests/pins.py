@@ -182,8 +182,9 @@ def _sig(z):
     return ez / (1.0 + ez)
 
 
-def _forward_bruteforce(x, Wr, br, Wgu, bgu, Wd, bd, k):
-    """Scalar loops, one token at a time; sigmoid via tanh.  Tiny shapes only."""
+def _forward_bruteforce(x, Wr, br, Wgu, bgu, Wd, bd, k, experts=None):
+    """Scalar loops, one token at a time; sigmoid via tanh.  Tiny shapes only.
+    experts: optional (lo, hi); only picks in [lo, hi) are summed."""
     X, WR, BR, WGU, BGU, WD, BD = (bf16_bits_to_f32(a).astype(np.float64).tolist()
                                    for a in (x, Wr, br, Wgu, bgu, Wd, bd))
     T, H = len(X), len(X[0])
@@ -199,6 +200,8 @@ def _forward_bruteforce(x, Wr, br, Wgu, bgu, Wd, bd, k):
         wsum = math.fsum(z)
         y = [0.0] * len(WD[0][0])
         for j, e in enumerate(chosen):
+            if experts is not None and not experts[0] <= e < experts[1]:
+                continue
             hid = []
             for i in range(I):
                 g = math.fsum([X[t][h] * WGU[e][h][2 * i] for h in range(H)] + [BGU[e][2 * i]])
@@ -305,6 +308,22 @@ def pin_skip_semantics(orc):
     assert np.isfinite(out["y"]).all()
 
 
+def pin_expert_ranges(orc):
+    """One expert-parallel rank's share: each range's partial y equals the
+    scalar brute force restricted to that range, and the partials of a
+    partition of [0, E) sum to the whole y."""
+    T, E, H, I, k = 4, 7, 16, 8, 3
+    inp = _tiny_inputs(31, T, E, H, I, 1.5)
+    full = _forward_bruteforce(*inp, k)
+    total = np.zeros_like(full)
+    for lo, hi in ((0, 2), (2, 3), (3, 7)):
+        part = orc.moe_forward(*inp, k=k, experts=(lo, hi))["y"]
+        ref = _forward_bruteforce(*inp, k, experts=(lo, hi))
+        assert np.abs(part - ref).max() <= 1e-12 * max(np.abs(full).max(), 1.0), (lo, hi)
+        total += part
+    assert np.abs(total - full).max() <= 1e-12 * np.abs(full).max()
+
+
 def pin_identity_glu_table(orc):
     """Wgu = 0, bgu = chosen (gate, up) pairs, Wd = identity, bd = 0:
     y = h(bgu) for every token and any routing, because the weights sum to 1."""
@@ -333,5 +352,5 @@ def pin_identity_glu_table(orc):
 
 
 ALL_PINS = [pin_glu, pin_topk, pin_router, pin_permutation, pin_forward_bruteforce,
-            pin_identical_experts, pin_structured_experts, pin_skip_semantics,
+            pin_identical_experts, pin_structured_experts, pin_skip_semantics, pin_expert_ranges,
             pin_identity_glu_table]

@@ -114,6 +114,25 @@ def test_stage_calls_validate(lib):
     assert lib.moe_combine(v, v, v, 4, 60, 2, v, None) == INVALID
 
 
+def _fwd_ep(lib, e_begin, n_local, T=8, H=64, E=8, k=2, I=64):
+    v = ctypes.c_void_p(FAKE)
+    return lib.moe_forward_ep(*([v] * 7), T, H, E, k, I, e_begin, n_local, v, None, None, v, 1 << 30, 0, None)
+
+
+@pytest.mark.parametrize("e_begin,n_local", [(-1, 2), (0, 0), (7, 2), (0, 9), (3, -1)])
+def test_forward_ep_rejects_bad_ranges(lib, e_begin, n_local):
+    assert _fwd_ep(lib, e_begin, n_local) == INVALID
+    assert b"local experts" in lib.moe_last_error()
+
+
+def test_forward_ep_accepts_every_valid_range(lib):
+    v = ctypes.c_void_p(FAKE)
+    for e_begin, n_local in ((0, 8), (0, 1), (7, 1), (2, 5)):
+        # T = 0: validated, nothing enqueued
+        assert lib.moe_forward_ep(*([v] * 7), 0, 64, 8, 2, 64, e_begin, n_local, v, None, None, None, 0, 0,
+                                  None) == OK
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     import importlib
     mod = importlib.import_module("moe_layer_route_amd.binding")

@@ -178,6 +178,56 @@ def test_forward_sweep(T, E, H, I, k, path):
     assert_y_close(host_f64(y), ref["y"], f"y {T}x{E}x{H}x{I}x{k} {path}")
 
 
+# ---------------------------------------------------------------------------
+# expert parallelism: one rank's share per call, partials summed on the host
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("T,E,H,I,k,ranges", [
+    (64, 32, 2880, 2880, 4, [(0, 16), (16, 32)]),
+    (37, 16, 136, 72, 4, [(0, 4), (4, 8), (8, 12), (12, 16)]),
+    (300, 8, 264, 128, 2, [(0, 1), (1, 5), (5, 8)]),            # uneven ranks
+    (5, 6, 40, 24, 2, [(0, 5), (5, 6)]),
+])
+def test_expert_parallel_ranks_sum_to_y(T, E, H, I, k, ranges, path):
+    _need_gpu()
+    inp = _small_inputs(T, E, H, I, k, seed=T + 3 * E)
+    x, Wr, br, Wgu, bgu, Wd, bd = [dev(a) for a in inp.arrays()]
+    ref = orc.moe_forward(*inp.arrays(), k=k)
+    total = np.zeros((T, H))
+    for lo, hi in ranges:
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        part = binding.moe_forward_ep(x, Wr, br, Wgu[lo:hi].contiguous(), bgu[lo:hi].contiguous(),
+                                      Wd[lo:hi].contiguous(), bd[lo:hi].contiguous(), lo, k=k,
+                                      topk_ids=ids, topk_w=w, path=path).double().cpu().numpy()
+        assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], ref["logits"], k)
+        want = orc.moe_forward(*inp.arrays(), k=k, experts=(lo, hi))["y"]
+        assert_y_close(part, want, f"rank [{lo},{hi}) {path}")
+        # tokens with no expert on this rank get exactly 0
+        none_here = ~((ref["ids"] >= lo) & (ref["ids"] < hi)).any(axis=1)
+        assert (part[none_here] == 0).all()
+        total += part
+    assert_y_close(total, ref["y"], f"sum of ranks {path}")
+
+
+def test_expert_parallel_never_reads_other_ranks_experts():
+    """A rank is handed only its own experts; NaN weights anywhere else in the
+    full model cannot reach its partial output."""
+    _need_gpu()
+    T, E, H, I, k = 40, 8, 136, 72, 2
+    inp = _small_inputs(T, E, H, I, k, seed=77)
+    x, Wr, br, Wgu, bgu, Wd, bd = [dev(a) for a in inp.arrays()]
+    lo, hi = 2, 5
+    poisoned = [t.clone() for t in (Wgu, bgu, Wd, bd)]
+    for t in poisoned:
+        t.view(torch.int16)[:lo] = 0x7FC0
+        t.view(torch.int16)[hi:] = 0x7FC0
+    part = binding.moe_forward_ep(x, Wr, br, *[t[lo:hi].contiguous() for t in poisoned], lo, k=k)
+    assert torch.isfinite(part).all()
+    want = orc.moe_forward(*inp.arrays(), k=k, experts=(lo, hi))["y"]
+    assert_y_close(part.double().cpu().numpy(), want, "rank [2,5)")
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_stage_intermediates(path):
     """gate_up and down alone against the oracle's h and o, matched through pos."""

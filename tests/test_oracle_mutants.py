@@ -85,7 +85,7 @@ def _perm_inclusive(ids, E):
     return cnt, off, rows, pos
 
 
-def _forward_multiply_by_zero(x, Wr, br, Wgu, bgu, Wd, bd, k, tokens=None, keep=False):
+def _forward_multiply_by_zero(x, Wr, br, Wgu, bgu, Wd, bd, k, tokens=None, keep=False, experts=None):
     """Runs every expert on every token and multiplies the unselected ones by 0."""
     ids, w, lg = orc.route(x, Wr, br, k)
     xs = orc.widen(x)
@@ -99,9 +99,9 @@ def _forward_multiply_by_zero(x, Wr, br, Wgu, bgu, Wd, bd, k, tokens=None, keep=
     return {"y": y, "ids": ids, "w": w, "logits": lg}
 
 
-def _forward_bias_outside(x, Wr, br, Wgu, bgu, Wd, bd, k, tokens=None, keep=False):
+def _forward_bias_outside(x, Wr, br, Wgu, bgu, Wd, bd, k, tokens=None, keep=False, experts=None):
     """Adds the down bias once per selected expert, outside the weighted sum."""
-    out = _real["moe_forward"](x, Wr, br, Wgu, bgu, Wd, bd, k, tokens, keep)
+    out = _real["moe_forward"](x, Wr, br, Wgu, bgu, Wd, bd, k, tokens, keep, experts)
     bdw = orc.widen(bd)
     for t in range(out["y"].shape[0]):
         for j in range(k):
@@ -110,9 +110,9 @@ def _forward_bias_outside(x, Wr, br, Wgu, bgu, Wd, bd, k, tokens=None, keep=Fals
     return out
 
 
-def _forward_no_weights(x, Wr, br, Wgu, bgu, Wd, bd, k, tokens=None, keep=False):
+def _forward_no_weights(x, Wr, br, Wgu, bgu, Wd, bd, k, tokens=None, keep=False, experts=None):
     ids, w, lg = orc.route(x, Wr, br, k)
-    out = _real["moe_forward"](x, Wr, br, Wgu, bgu, Wd, bd, k, tokens, keep)
+    out = _real["moe_forward"](x, Wr, br, Wgu, bgu, Wd, bd, k, tokens, keep, experts)
     # re-sum the expert outputs without the routing weights
     xs = orc.widen(x)
     y = np.zeros_like(out["y"])
@@ -122,6 +122,18 @@ def _forward_no_weights(x, Wr, br, Wgu, bgu, Wd, bd, k, tokens=None, keep=False)
             y[t] += orc.expert_mlp(xs[t:t + 1], orc.widen(Wgu[e]), orc.widen(bgu[e]), orc.widen(Wd[e]), orc.widen(bd[e]))[2][0]
     out["y"] = y
     return out
+
+
+def _forward_range_inclusive(x, Wr, br, Wgu, bgu, Wd, bd, k, tokens=None, keep=False, experts=None):
+    """An expert range that also takes its end expert."""
+    if experts is not None:
+        experts = (experts[0], min(experts[1] + 1, Wr.shape[0]))
+    return _real["moe_forward"](x, Wr, br, Wgu, bgu, Wd, bd, k, tokens, keep, experts)
+
+
+def _forward_range_ignored(x, Wr, br, Wgu, bgu, Wd, bd, k, tokens=None, keep=False, experts=None):
+    """Every rank returns the whole y."""
+    return _real["moe_forward"](x, Wr, br, Wgu, bgu, Wd, bd, k, tokens, keep)
 
 
 def _widen_truncating(bits):
@@ -156,6 +168,8 @@ MUTANTS = {
     "forward_multiply_by_zero": ("moe_forward", _forward_multiply_by_zero),
     "forward_down_bias_outside_sum": ("moe_forward", _forward_bias_outside),
     "forward_no_routing_weights": ("moe_forward", _forward_no_weights),
+    "forward_expert_range_inclusive": ("moe_forward", _forward_range_inclusive),
+    "forward_expert_range_ignored": ("moe_forward", _forward_range_ignored),
     "widen_drops_a_bit": ("widen", _widen_truncating),
 }
 
