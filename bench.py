@@ -161,6 +161,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ep", type=int, default=1,
+                    help="also time one expert-parallel rank's share of W ranks: experts [0, E/W), "
+                         "all tokens routed (reported in ep_rank_share, not in value)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy, the reference kernel "
                          "that scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -295,6 +298,36 @@ def main(argv=None):
     layer_flops = _alg_flops_layer(cfg)
     step_s = ms_per_step * 1e-3
 
+    ep_share = None
+    if args.ep > 1:
+        if E % args.ep:
+            print(f"bench.py: E={E} is not divisible by --ep {args.ep}", file=sys.stderr)
+            return 2
+        nl = E // args.ep
+        y_part = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        local = [t[:nl] for t in (Wgu, bgu, Wd, bd)]
+
+        def ep_step():
+            binding.moe_forward_ep(x, Wr, br, *local, 0, k=k, y_partial=y_part, workspace=ws, path=args.path,
+                                   stream=stream)
+
+        for _ in range(args.warmup):
+            ep_step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            ep_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ep_ms = e0.elapsed_time(e1) / args.steps
+        local_slots = int(((ids >= 0) & (ids < nl)).sum().item())
+        ep_share = {"ranks": args.ep, "local_experts": nl, "local_slots": local_slots, "ms_per_step": ep_ms,
+                    "tokens_per_s_per_rank": T / (ep_ms * 1e-3)}
+        print(f"[bench] expert-parallel rank share ({nl} of {E} experts): {ep_ms * 1e3:.1f} us/step",
+              file=sys.stderr, flush=True)
+
     out = {
         "metric": METRIC,
         "value": T / step_s,
@@ -319,6 +352,7 @@ def main(argv=None):
         "cold_latency_us": cold,
         "graph_ms_per_step": graph_ms,
         "achievable": _achievable(torch),
+        "ep_rank_share": ep_share,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
