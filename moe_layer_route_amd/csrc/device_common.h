@@ -22,15 +22,15 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// float32 -> bfloat16, round to nearest even; NaN stays NaN (quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// float32 -> bfloat16, round to nearest even (the gfx950 conversion
+// instruction, v_cvt_pk_bf16_f32); NaN stays NaN (quiet).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // v_perm_b32 byte selection over {hi:a, lo:b}
@@ -76,11 +76,13 @@ __device__ __forceinline__ void transpose8x8_b16(const u32x4_t (&in)[8], u32x4_t
   }
 }
 
-// Clamped interleaved GLU of one (gate, up) pair, float32.
+// Clamped interleaved GLU of one (gate, up) pair, float32.  The logistic
+// uses the hardware exponential and reciprocal (about 1 ulp each; h is then
+// rounded to bf16).
 __device__ __forceinline__ float clamped_glu(float gate, float up) {
   const float g = fminf(gate, 7.0f);
   const float u = fminf(fmaxf(up, -7.0f), 7.0f);
-  const float s = 1.0f / (1.0f + __expf(-1.702f * g));
+  const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * g));
   return (u + 1.0f) * (g * s);
 }
 
