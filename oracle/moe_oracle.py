@@ -34,6 +34,9 @@ Readings where the pages are silent (each is listed in the design doc):
       (down), i.e. y = sum_j w_j * (h_j @ Wd[e_j] + bd[e_j]);
 * R5  the clamped gate value is used in both factors of gate*sigmoid(1.702*gate);
       up is clamped first, then 1 is added.
+
+The MXFP4 weight format (section 5 of the same page) and its readings M1-M3
+are stated next to its functions below.
 """
 from __future__ import annotations
 
@@ -153,16 +156,23 @@ def moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k: int, tokens=None, keep=False, ex
     lies in that range -- one expert-parallel rank's share (section 2 of the
     Phase 19 page: expert parallelism filters by expert range and sums the
     ranks' partial outputs).  The weights stay indexed by global expert id."""
+    def weights(e):
+        return widen(Wgu[e]), widen(bgu[e]), widen(Wd[e]), widen(bd[e])
+    return _forward(x, Wr, br, weights, Wgu.shape[2], Wd.shape[2], k, tokens, keep, experts)
+
+
+def _forward(x, Wr, br, weights, I2, Hout, k, tokens=None, keep=False, experts=None):
+    """The sparse forward over a weight provider: weights(e) returns expert
+    e's (Wgu [H][2I], bgu [2I], Wd [I][H], bd [H]) as float64 in x.W form."""
     ids, w, lg = route(x if tokens is None else x[np.asarray(tokens)], Wr, br, k)
     xs = widen(x if tokens is None else x[np.asarray(tokens)])
     T, H = xs.shape
     E = Wr.shape[0]
-    y = np.zeros((T, Wd.shape[2]), dtype=np.float64)
-    I2 = Wgu.shape[2]
+    y = np.zeros((T, Hout), dtype=np.float64)
     if keep:
         u_all = np.zeros((T * k, I2))
         h_all = np.zeros((T * k, I2 // 2))
-        o_all = np.zeros((T * k, Wd.shape[2]))
+        o_all = np.zeros((T * k, Hout))
     flat = ids.reshape(-1)
     e_lo, e_hi = (0, E) if experts is None else experts
     for e in range(e_lo, e_hi):
@@ -170,7 +180,7 @@ def moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k: int, tokens=None, keep=False, ex
         if slots.size == 0:
             continue               # skipped, never multiplied by zero
         toks = slots // k
-        u, h, o = expert_mlp(xs[toks], widen(Wgu[e]), widen(bgu[e]), widen(Wd[e]), widen(bd[e]))
+        u, h, o = expert_mlp(xs[toks], *weights(e))
         ws = w.reshape(-1)[slots]
         np.add.at(y, toks, ws[:, None] * o)
         if keep:
@@ -179,6 +189,94 @@ def moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k: int, tokens=None, keep=False, ex
     if keep:
         out.update(u=u_all, h=h_all, o=o_all)
     return out
+
+
+# --------------------------------------------------------------------------
+# MXFP4 expert weights (section 5 of the Phase 19 page, "MXFP4 W4A16": the
+# weights are 4-bit E2M1 values with one UE8M0 power-of-two scale per 32
+# values; activations stay bf16).  Readings (listed in the design doc):
+#   M1  a block is 32 consecutive values along the contraction dimension K
+#       (the dimension a dot product runs over), so the weights are stored
+#       K-contiguous: codes [E][N][K/2] (byte i of row n holds k = 2i in bits
+#       0-3 and k = 2i+1 in bits 4-7), scales [E][N][K/32];
+#   M2  the quantiser is the microscaling formats' reference conversion: per
+#       block, X = 2^(floor(log2(max|v|)) - 2) (2 is the largest exponent of
+#       E2M1, whose largest value is 6 = 1.5 * 2^2), each v / X rounded to the
+#       nearest E2M1 value with ties to the even code and magnitudes above 6
+#       saturated to 6; an all-zero block takes X = 2^-127 (code 0 stored);
+#       the sign bit of a code is the sign bit of v;
+#   M3  dequantisation is exact: value = E2M1(code) * 2^(scale - 127); scale
+#       byte 255 is NaN.
+# --------------------------------------------------------------------------
+E2M1_EMAX = 2
+
+
+def e2m1_decode(code: int) -> float:
+    """Value of a 4-bit E2M1 code: bit 3 sign, bits 2..1 exponent (bias 1),
+    bit 0 mantissa; exponent 0 is subnormal (0 or 0.5)."""
+    sign = -1.0 if (code >> 3) & 1 else 1.0
+    ex = (code >> 1) & 3
+    man = code & 1
+    mag = 0.5 * man if ex == 0 else (1.0 + 0.5 * man) * 2.0 ** (ex - 1)
+    return sign * mag
+
+
+E2M1_VALUES = np.array([e2m1_decode(c) for c in range(16)], dtype=np.float64)
+
+
+def ue8m0_decode(e) -> np.ndarray:
+    """2^(e - 127) for scale bytes e; 255 is NaN."""
+    e = np.asarray(e, dtype=np.int64)
+    v = np.ldexp(1.0, e - 127)
+    return np.where(e == 255, np.nan, v)
+
+
+def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """codes uint8 [..., N, K/2] and scales uint8 [..., N, K/32] -> float64 [..., N, K]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    q = np.empty(codes.shape[:-1] + (2 * codes.shape[-1],), dtype=np.float64)
+    q[..., 0::2] = E2M1_VALUES[codes & 15]
+    q[..., 1::2] = E2M1_VALUES[codes >> 4]
+    sc = np.repeat(ue8m0_decode(scales), 32, axis=-1)
+    return q * sc
+
+
+def mxfp4_quantize(w: np.ndarray):
+    """float [..., N, K] (K % 32 == 0) -> (codes uint8 [..., N, K/2], scales uint8 [..., N, K/32])."""
+    w = np.asarray(w, dtype=np.float64)
+    K = w.shape[-1]
+    assert K % 32 == 0
+    blk = w.reshape(w.shape[:-1] + (K // 32, 32))
+    amax = np.abs(blk).max(axis=-1)
+    _, p = np.frexp(amax)                     # amax = m * 2^p, m in [0.5, 1)
+    shared = np.where(amax > 0, p - 1 - E2M1_EMAX, -127)
+    shared = np.clip(shared, -127, 127)
+    X = np.ldexp(1.0, shared)[..., None]
+    v = np.abs(blk) / X                        # exact: X is a power of two
+    mags = E2M1_VALUES[:8]
+    dist = np.abs(v[..., None] - mags)         # [..., 32, 8]
+    best = dist.min(axis=-1, keepdims=True)
+    # among the nearest magnitudes take the even code (ties to even)
+    cand = (dist == best)
+    even = cand & (np.arange(8) % 2 == 0)
+    mag_code = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    sign = np.signbit(blk).astype(np.int64)
+    code = (sign << 3) | mag_code
+    code = code.reshape(w.shape)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    scales = (shared + 127).astype(np.uint8)
+    return packed, scales
+
+
+def moe_forward_mxfp4(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k: int, tokens=None, keep=False,
+                      experts=None):
+    """The forward with MXFP4 expert weights (W4A16): gate_up codes [E][2I][H/2]
+    and scales [E][2I][H/32], down codes [E][H][I/2] and scales [E][H][I/32];
+    the weights are dequantised exactly and the rest is moe_forward."""
+    def weights(e):
+        return (mxfp4_dequantize(Wgu_q[e], Wgu_s[e]).T, widen(bgu[e]),
+                mxfp4_dequantize(Wd_q[e], Wd_s[e]).T, widen(bd[e]))
+    return _forward(x, Wr, br, weights, Wgu_q.shape[1], Wd_q.shape[1], k, tokens, keep, experts)
 
 
 # --------------------------------------------------------------------------

@@ -351,6 +351,130 @@ def pin_identity_glu_table(orc):
     assert (y[:, len(pairs):] == 0.0).all()
 
 
+# ---------------------------------------------------------------------------
+# MXFP4 weights (section 5 of the page: E2M1 values with one UE8M0 scale per
+# 32 values).  The element and scale tables are those of the OCP microscaling
+# formats; the nearest-value and forward pins recompute by brute force.
+# ---------------------------------------------------------------------------
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def pin_e2m1_table(orc):
+    got = [float(orc.e2m1_decode(c)) for c in range(16)]
+    assert got == E2M1_TABLE, got
+    assert [math.copysign(1.0, v) for v in got] == [math.copysign(1.0, v) for v in E2M1_TABLE]
+    assert (np.asarray(orc.E2M1_VALUES) == np.array(E2M1_TABLE)).all()
+
+
+def pin_ue8m0(orc):
+    e = np.array([0, 1, 100, 126, 127, 128, 200, 254, 255])
+    got = orc.ue8m0_decode(e)
+    want = [2.0 ** -127, 2.0 ** -126, 2.0 ** -27, 0.5, 1.0, 2.0, 2.0 ** 73, 2.0 ** 127]
+    assert list(got[:-1]) == want, got
+    assert math.isnan(got[-1])
+
+
+def pin_mxfp4_layout(orc):
+    """Low nibble = even k, high nibble = odd k; one scale per 32 consecutive k."""
+    codes = np.zeros((2, 32), np.uint8)          # N = 2 rows of K = 64
+    scales = np.full((2, 2), 127, np.uint8)
+    codes[0, 0] = 0x21                           # k0: code 1 (0.5), k1: code 2 (1.0)
+    codes[0, 16] = 0xF7                          # k32: code 7 (6), k33: code 15 (-6)
+    codes[1, 15] = 0x9C                          # k30: code 12 (-2), k31: code 9 (-0.5)
+    scales[0, 1] = 125                           # block 1 of row 0 scaled by 1/4
+    scales[1, 0] = 130                           # block 0 of row 1 scaled by 8
+    d = orc.mxfp4_dequantize(codes, scales)
+    assert d.shape == (2, 64)
+    assert (d[0, 0], d[0, 1], d[0, 32], d[0, 33]) == (0.5, 1.0, 1.5, -1.5), d[0, [0, 1, 32, 33]]
+    assert (d[1, 30], d[1, 31]) == (-16.0, -4.0), d[1, 30:32]
+    nz = np.ones_like(d, bool)
+    nz[0, [0, 1, 32, 33]] = False
+    nz[1, [30, 31]] = False
+    assert (d[nz] == 0).all()
+
+
+def pin_mxfp4_quantize_rne(orc):
+    """Ties to the even code, saturation at 6, the shared exponent from the block maximum."""
+    v = [7.9, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 5.5, 0.2, 0.3, -0.25, -0.75, -5.0, 6.0, 4.4]
+    want = [7, 0, 2, 2, 4, 4, 6, 6, 7, 0, 1, 8, 10, 14, 7, 6]
+    blk = np.zeros((1, 32))
+    blk[0, :16] = v
+    codes, scales = orc.mxfp4_quantize(blk)
+    got = [int(codes[0, i // 2] >> (4 * (i % 2))) & 15 for i in range(16)]
+    assert got == want, got
+    assert scales[0, 0] == 127, scales                       # max 7.9: 2^(2 - 2) = 1
+    # a block whose maximum is 6 * 2^-8 has scale 2^-8 and codes 7 for it
+    blk2 = np.zeros((1, 32))
+    blk2[0, 5] = 6 * 2.0 ** -8
+    blk2[0, 6] = -3 * 2.0 ** -8
+    c2, s2 = orc.mxfp4_quantize(blk2)
+    assert s2[0, 0] == 127 - 8 and (c2[0, 2] >> 4) == 7 and (c2[0, 3] & 15) == 13, (s2, c2)
+    # an all-zero block: scale 2^-127, all codes 0; a value far below the
+    # block maximum rounds to zero
+    c3, s3 = orc.mxfp4_quantize(np.zeros((1, 32)))
+    assert s3[0, 0] == 0 and (c3 == 0).all()
+    blk4 = np.zeros((1, 32))
+    blk4[0, 0], blk4[0, 1] = 1.0, 1.0 / 17
+    c4, s4 = orc.mxfp4_quantize(blk4)
+    assert s4[0, 0] == 125 and (c4[0, 0] & 15) == 6 and (c4[0, 0] >> 4) == 0, (s4, c4)
+
+
+def pin_mxfp4_nearest(orc):
+    """Every code is a nearest E2M1 value of v / X (ties: even code), with X
+    = 2^(floor(log2 max|v|) - 2) recomputed with math.frexp; dequantising
+    reproduces v whenever v / X is itself an E2M1 value."""
+    rng = np.random.default_rng(41)
+    w = rng.normal(0, 1, (6, 128)) * np.exp2(rng.integers(-20, 8, (6, 1)))
+    w[0, :32] = 0.0
+    w[1, 32:64] = rng.choice(E2M1_TABLE, 32) * 2.0 ** -5   # exactly representable block
+    w[1, 40] = 6 * 2.0 ** -5
+    codes, scales = orc.mxfp4_quantize(w)
+    d = orc.mxfp4_dequantize(codes, scales)
+    for r in range(w.shape[0]):
+        for b in range(4):
+            blk = w[r, 32 * b:32 * b + 32]
+            amax = max(abs(float(t)) for t in blk)
+            if amax == 0.0:
+                xe = -127
+            else:
+                xe = max(-127, min(127, math.frexp(amax)[1] - 1 - 2))
+            assert scales[r, b] == xe + 127, (r, b, scales[r, b], xe)
+            X = 2.0 ** xe
+            for i in range(32):
+                val = float(blk[i])
+                c = (int(codes[r, 16 * b + i // 2]) >> (4 * (i % 2))) & 15
+                dist = [abs(val / X - t) for t in E2M1_TABLE]
+                best = min(dist)
+                ties = [cc for cc in range(16) if dist[cc] == best and math.copysign(1, E2M1_TABLE[cc]) == math.copysign(1, val)]
+                pick = [cc for cc in ties if cc % 2 == 0] or ties
+                assert c == pick[0], (r, b, i, val / X, c, pick)
+    assert (d[1, 32:64] == w[1, 32:64]).all()
+
+
+def _tiny_mxfp4(orc, seed, T, E, H, I, scale):
+    """Tiny inputs with MXFP4 expert weights, and the same weights as bf16
+    bits in x.W form (the dequantised values are exact in bf16)."""
+    x, Wr, br, Wgu, bgu, Wd, bd = _tiny_inputs(seed, T, E, H, I, scale)
+    rng = np.random.default_rng(seed + 7)
+    gu_q, gu_s = orc.mxfp4_quantize(rng.normal(0, 0.3, (E, 2 * I, H)))
+    d_q, d_s = orc.mxfp4_quantize(rng.normal(0, 0.3, (E, H, I)))
+    Wgu_b = _bf(np.transpose(orc.mxfp4_dequantize(gu_q, gu_s), (0, 2, 1)))
+    Wd_b = _bf(np.transpose(orc.mxfp4_dequantize(d_q, d_s), (0, 2, 1)))
+    assert (bf16_bits_to_f32(Wgu_b) == np.transpose(orc.mxfp4_dequantize(gu_q, gu_s), (0, 2, 1))).all()
+    return (x, Wr, br, gu_q, gu_s, bgu, d_q, d_s, bd), (x, Wr, br, Wgu_b, bgu, Wd_b, bd)
+
+
+def pin_mxfp4_forward(orc):
+    """The MXFP4 forward equals the scalar brute force on the dequantised weights."""
+    for n, (T, E, H, I, k) in enumerate([(3, 4, 32, 32, 2), (4, 6, 64, 32, 3)]):
+        q_args, b_args = _tiny_mxfp4(orc, 300 + n, T, E, H, I, 1.5)
+        ref = _forward_bruteforce(*b_args, k)
+        got = orc.moe_forward_mxfp4(*q_args, k=k)["y"]
+        assert got.shape == ref.shape
+        assert np.abs(got - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max()), n
+
+
 ALL_PINS = [pin_glu, pin_topk, pin_router, pin_permutation, pin_forward_bruteforce,
             pin_identical_experts, pin_structured_experts, pin_skip_semantics, pin_expert_ranges,
-            pin_identity_glu_table]
+            pin_identity_glu_table, pin_e2m1_table, pin_ue8m0, pin_mxfp4_layout, pin_mxfp4_quantize_rne,
+            pin_mxfp4_nearest, pin_mxfp4_forward]

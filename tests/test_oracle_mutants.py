@@ -9,7 +9,8 @@ import pins
 
 _real = {n: getattr(orc, n) for n in ("clamped_glu", "router_logits", "select_topk",
                                       "routing_weights", "expert_mlp", "expert_permutation",
-                                      "moe_forward", "widen")}
+                                      "moe_forward", "widen", "mxfp4_quantize", "mxfp4_dequantize",
+                                      "moe_forward_mxfp4", "ue8m0_decode", "e2m1_decode")}
 
 
 def _glu(gate_sel=0, up_sel=1, alpha=1.702, glim=(-np.inf, 7.0), ulim=(-7.0, 7.0), plus=1.0,
@@ -142,7 +143,76 @@ def _widen_truncating(bits):
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def _e2m1_table_typo():
+    t = np.array(orc.E2M1_VALUES, copy=True)
+    t[5], t[13] = 2.5, -2.5
+    return t
+
+
+def _e2m1_decode_bias0(code):
+    return 2.0 * _real["e2m1_decode"](code)
+
+
+def _ue8m0_bias128(e):
+    return _real["ue8m0_decode"](np.asarray(e) - 1)
+
+
+def _dequant_nibbles_swapped(codes, scales):
+    c = np.asarray(codes, np.uint8)
+    return _real["mxfp4_dequantize"](((c & 15) << 4) | (c >> 4), scales)
+
+
+def _dequant_scales_tiled(codes, scales):
+    codes = np.asarray(codes, dtype=np.uint8)
+    q = np.empty(codes.shape[:-1] + (2 * codes.shape[-1],))
+    q[..., 0::2] = orc.E2M1_VALUES[codes & 15]
+    q[..., 1::2] = orc.E2M1_VALUES[codes >> 4]
+    return q * np.tile(orc.ue8m0_decode(scales), 32)
+
+
+def _quant_variant(ties="even", emax=2, ceil_exp=False):
+    def f(w):
+        w = np.asarray(w, dtype=np.float64)
+        K = w.shape[-1]
+        blk = w.reshape(w.shape[:-1] + (K // 32, 32))
+        amax = np.abs(blk).max(axis=-1)
+        _, p = np.frexp(amax)
+        e = p if ceil_exp else p - 1
+        shared = np.clip(np.where(amax > 0, e - emax, -127), -127, 127)
+        X = np.ldexp(1.0, shared)[..., None]
+        v = np.abs(blk) / X
+        mags = orc.E2M1_VALUES[:8]
+        dist = np.abs(v[..., None] - mags)
+        best = dist.min(axis=-1, keepdims=True)
+        cand = dist == best
+        if ties == "even":
+            pick = cand & (np.arange(8) % 2 == 0)
+            code = np.where(pick.any(-1), pick.argmax(-1), cand.argmax(-1))
+        else:                                     # ties to the larger magnitude
+            code = 7 - cand[..., ::-1].argmax(-1)
+        code = ((np.signbit(blk).astype(np.int64) << 3) | code).reshape(w.shape)
+        return (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8), (shared + 127).astype(np.uint8)
+    return f
+
+
+def _forward_mxfp4_untransposed(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k, tokens=None, keep=False,
+                                experts=None):
+    def weights(e):
+        return (orc.mxfp4_dequantize(Wgu_q[e], Wgu_s[e]).reshape(Wgu_q.shape[2] * 2, -1), orc.widen(bgu[e]),
+                orc.mxfp4_dequantize(Wd_q[e], Wd_s[e]).reshape(Wd_q.shape[2] * 2, -1), orc.widen(bd[e]))
+    return orc._forward(x, Wr, br, weights, Wgu_q.shape[1], Wd_q.shape[1], k, tokens, keep, experts)
+
+
 MUTANTS = {
+    "e2m1_table_typo": ("E2M1_VALUES", _e2m1_table_typo()),
+    "e2m1_exponent_bias_0": ("e2m1_decode", _e2m1_decode_bias0),
+    "ue8m0_bias_128": ("ue8m0_decode", _ue8m0_bias128),
+    "mxfp4_nibbles_swapped": ("mxfp4_dequantize", _dequant_nibbles_swapped),
+    "mxfp4_scales_tiled": ("mxfp4_dequantize", _dequant_scales_tiled),
+    "mxfp4_ties_away": ("mxfp4_quantize", _quant_variant(ties="away")),
+    "mxfp4_emax_3": ("mxfp4_quantize", _quant_variant(emax=3)),
+    "mxfp4_exponent_rounded_up": ("mxfp4_quantize", _quant_variant(ceil_exp=True)),
+    "mxfp4_forward_weights_untransposed": ("moe_forward_mxfp4", _forward_mxfp4_untransposed),
     "glu_swap_gate_up": ("clamped_glu", _glu(gate_sel=1, up_sel=0)),
     "glu_alpha_1": ("clamped_glu", _glu(alpha=1.0)),
     "glu_alpha_1.8": ("clamped_glu", _glu(alpha=1.8)),
