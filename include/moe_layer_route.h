@@ -244,6 +244,68 @@ MOE_API int moe_down(const void* h, const void* Wd, const void* bd,
 MOE_API int moe_combine(const float* o, const int32_t* pos, const float* topk_w,
                 int64_t T, int32_t H, int32_t k, void* y, void* stream);
 
+/*
+ * MXFP4 expert weights (W4A16) -- xserv "Phase 19: gpt-oss-20b MoE support",
+ * section 5: the expert weights are 4-bit E2M1 values with one UE8M0
+ * (power-of-two) scale per 32 values; activations, biases, the router and
+ * every output stay as in moe_forward.
+ *
+ * Format, for a weight with contraction dimension K and N output columns
+ * (gate_up: K = H, N = 2I; down: K = I, N = H), stored K-contiguous:
+ *   codes  uint8 [E][N][K/2]   row n holds the K values of output column n,
+ *                              two per byte: k = 2i in bits 0-3, k = 2i+1 in
+ *                              bits 4-7.  E2M1 code: bit 3 sign, bits 2-1
+ *                              exponent (bias 1), bit 0 mantissa; magnitudes
+ *                              0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ *   scales uint8 [E][N][K/32]  the 32 values k = 32b .. 32b+31 of column n are
+ *                              multiplied by 2^(scales[e][n][b] - 127); 255 is
+ *                              NaN.
+ * The weight value is E2M1(code) * 2^(scale - 127), exactly.  Requires
+ * H % 32 == 0 and I % 32 == 0; codes and scales 16-byte aligned.
+ */
+
+/*
+ * moe_quantize_mxfp4 -- converts bf16 weights W [E][K][N] (x.W form, as in
+ * moe_forward) to the MXFP4 format above, one 32-value block at a time: the
+ * shared exponent is floor(log2(max |v|)) - 2 clamped to [-127, 127] (-127
+ * for an all-zero block), and each v / 2^exponent is rounded to the nearest
+ * E2M1 value, ties to the even code, magnitudes above 6 saturated to 6; the
+ * sign bit of a code is the sign bit of v.  (The microscaling formats'
+ * reference conversion.)  K % 32 == 0, N % 8 == 0.
+ *   W       bf16 [E][K][N]   in
+ *   codes   uint8 [E][N][K/2]   out
+ *   scales  uint8 [E][N][K/32]  out
+ */
+MOE_API int moe_quantize_mxfp4(const void* W, int32_t E, int32_t K, int32_t N, void* codes, void* scales,
+                               void* stream);
+
+/*
+ * moe_forward_mxfp4 -- moe_forward with MXFP4 expert weights:
+ *   Wgu_q uint8 [E][2I][H/2], Wgu_s uint8 [E][2I][H/32]   gate_up (columns
+ *                          interleaved gate0, up0, gate1, ... as in moe_forward)
+ *   Wd_q  uint8 [E][H][I/2],  Wd_s  uint8 [E][H][I/32]    down
+ * Every other argument, the workspace size (moe_workspace_bytes) and the
+ * result's definition are those of moe_forward with the weights replaced by
+ * their exact dequantised values; the dequantised weights are bf16 operands
+ * of the same float32-accumulating products.  The expert kernels stream the
+ * 4-bit weights (one pass over each live expert's weights per 32 rows).
+ */
+MOE_API int moe_forward_mxfp4(const void* x, const void* Wr, const void* br,
+                              const void* Wgu_q, const void* Wgu_s, const void* bgu,
+                              const void* Wd_q, const void* Wd_s, const void* bd,
+                              int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                              void* y, int32_t* topk_ids_out, float* topk_w_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage calls of moe_forward_mxfp4: moe_gate_up and moe_down with MXFP4
+ * weights (same inputs, outputs and layouts otherwise). */
+MOE_API int moe_gate_up_mxfp4(const void* x, const void* Wgu_q, const void* Wgu_s, const void* bgu,
+                              const int32_t* cnt, const int32_t* off, const int32_t* rows,
+                              int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, void* h, void* stream);
+MOE_API int moe_down_mxfp4(const void* h, const void* Wd_q, const void* Wd_s, const void* bd,
+                           const int32_t* cnt, const int32_t* off,
+                           int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, float* o, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -323,6 +323,119 @@ int moe_down(const void* h, const void* Wd, const void* bd, const int32_t* cnt, 
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 expert weights
+// ---------------------------------------------------------------------------
+static int check_mx_dims(const char* fn, int32_t H, int32_t I) {
+  if (H % 32 != 0 || I % 32 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: H=%d and I=%d must be multiples of 32 (MXFP4 blocks)", fn, H, I);
+  return MOE_OK;
+}
+
+int moe_quantize_mxfp4(const void* W, int32_t E, int32_t K, int32_t N, void* codes, void* scales, void* stream) {
+  const char* fn = "moe_quantize_mxfp4";
+  if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", fn, E, MOE_MAX_E);
+  if (K < 32 || K > MOE_MAX_DIM || K % 32 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: K=%d must be a multiple of 32 in [32, %d]", fn, K, MOE_MAX_DIM);
+  if (N < 8 || N > 2 * MOE_MAX_DIM || N % 8 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: N=%d must be a multiple of 8 in [8, %d]", fn, N, 2 * MOE_MAX_DIM);
+  CHECK_PTR(W, 2);
+  CHECK_PTR(codes, 16);
+  CHECK_PTR(scales, 1);
+  if (int st = hip_status(fn, moe::launch_mxfp4_quantize(W, E, K, N, codes, scales, (hipStream_t)stream))) return st;
+  return ok();
+}
+
+int moe_forward_mxfp4(const void* x, const void* Wr, const void* br, const void* Wgu_q, const void* Wgu_s,
+                      const void* bgu, const void* Wd_q, const void* Wd_s, const void* bd, int64_t T, int32_t H,
+                      int32_t E, int32_t k, int32_t I, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_forward_mxfp4";
+  if (int st = check_dims(fn, T, H, E, k, I)) return st;
+  if (int st = check_mx_dims(fn, H, I)) return st;
+  CHECK_PTR(x, 16);
+  CHECK_PTR(Wr, 16);
+  CHECK_PTR(br, 2);
+  CHECK_PTR(Wgu_q, 16);
+  CHECK_PTR(Wgu_s, 16);
+  CHECK_PTR(bgu, 4);
+  CHECK_PTR(Wd_q, 16);
+  CHECK_PTR(Wd_s, 16);
+  CHECK_PTR(bd, 4);
+  CHECK_PTR(y, 16);
+  if (topk_ids_out && !aligned(topk_ids_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_ids_out is not 4-byte aligned", fn);
+  if (topk_w_out && !aligned(topk_w_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_w_out is not 4-byte aligned", fn);
+  if (T == 0) return ok();
+  const Layout L = layout(T, H, E, k, I);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, L.total);
+  if (!aligned(workspace, 256))
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.cnt);
+  int32_t* off = reinterpret_cast<int32_t*>(ws + L.off);
+  int32_t* rows = reinterpret_cast<int32_t*>(ws + L.rows);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+  void* h = ws + L.h;
+  float* o = reinterpret_cast<float*>(ws + L.o);
+  hipStream_t s = (hipStream_t)stream;
+
+  if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, ids, w, MOE_ROUTE_AUTO, s))) return st;
+  if (int st = hip_status(fn, moe::launch_permute(ids, T, E, k, cnt, off, rows, pos, s))) return st;
+  if (int st = hip_status(fn, moe::launch_mxfp4_gate_up(x, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, E, k, I, h, s)))
+    return st;
+  if (int st = hip_status(fn, moe::launch_mxfp4_down(h, Wd_q, Wd_s, bd, cnt, off, T, H, E, k, I, o, s))) return st;
+  if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s))) return st;
+  return ok();
+}
+
+int moe_gate_up_mxfp4(const void* x, const void* Wgu_q, const void* Wgu_s, const void* bgu, const int32_t* cnt,
+                      const int32_t* off, const int32_t* rows, int64_t T, int32_t H, int32_t E, int32_t k,
+                      int32_t I, void* h, void* stream) {
+  const char* fn = "moe_gate_up_mxfp4";
+  if (int st = check_dims(fn, T, H, E, k, I)) return st;
+  if (int st = check_mx_dims(fn, H, I)) return st;
+  CHECK_PTR(x, 16);
+  CHECK_PTR(Wgu_q, 16);
+  CHECK_PTR(Wgu_s, 16);
+  CHECK_PTR(bgu, 4);
+  CHECK_PTR(cnt, 4);
+  CHECK_PTR(off, 4);
+  CHECK_PTR(rows, 4);
+  CHECK_PTR(h, 16);
+  if (T == 0) return ok();
+  if (int st = hip_status(fn, moe::launch_mxfp4_gate_up(x, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, E, k, I, h,
+                                                        (hipStream_t)stream)))
+    return st;
+  return ok();
+}
+
+int moe_down_mxfp4(const void* h, const void* Wd_q, const void* Wd_s, const void* bd, const int32_t* cnt,
+                   const int32_t* off, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, float* o,
+                   void* stream) {
+  const char* fn = "moe_down_mxfp4";
+  if (int st = check_dims(fn, T, H, E, k, I)) return st;
+  if (int st = check_mx_dims(fn, H, I)) return st;
+  CHECK_PTR(h, 16);
+  CHECK_PTR(Wd_q, 16);
+  CHECK_PTR(Wd_s, 16);
+  CHECK_PTR(bd, 4);
+  CHECK_PTR(cnt, 4);
+  CHECK_PTR(off, 4);
+  CHECK_PTR(o, 16);
+  if (T == 0) return ok();
+  if (int st = hip_status(fn, moe::launch_mxfp4_down(h, Wd_q, Wd_s, bd, cnt, off, T, H, E, k, I, o,
+                                                     (hipStream_t)stream)))
+    return st;
+  return ok();
+}
+
 int moe_combine(const float* o, const int32_t* pos, const float* topk_w, int64_t T, int32_t H, int32_t k,
                 void* y, void* stream) {
   const char* fn = "moe_combine";

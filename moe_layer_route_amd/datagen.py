@@ -26,6 +26,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 X_ID, WR_ID, BR_ID, WGU_ID, BGU_ID, WD_ID, BD_ID, PERM_ID = 1, 2, 3, 4, 5, 6, 7, 8
+MXGU_ID, MXD_ID = 9, 10
 
 # Scale of x that puts about 5% of the gate/up pre-activations past the +-7
 # clamp for weights N(0, 0.02) and biases N(0, 0.01) at H = 2880: a
@@ -200,3 +201,74 @@ def small_config(T: int, E: int, H: int, I: int, k: int, x_scale: float = X_SCAL
 def scale_for_hidden(H: int) -> float:
     """x scale that keeps the pre-activation spread of the full-size configs at hidden size H."""
     return X_SCALE_CLAMP5 * math.sqrt(2880.0 / H)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 expert weights drawn directly as codes and scales (no quantisation
+# arithmetic here).  The distributions are those that N(0, 0.02) weights take
+# in the format: magnitude codes 0..7 with the frequencies below, an even
+# sign, and the block scale byte 120 (2^-7) for 92.6% of the blocks, 121 for
+# 5.6% and 119 for 1.8%; the values then have a standard deviation of about
+# 0.02, like the bf16 workloads.
+# ---------------------------------------------------------------------------
+MX_MAG_FREQ = (0.0811, 0.1587, 0.1474, 0.1312, 0.1620, 0.1505, 0.1183, 0.0508)
+MX_SCALE_FREQ = {119: 0.018, 120: 0.926, 121: 0.056}
+
+
+def _byte_table():
+    """65536-entry table: a uniform 16-bit draw -> one code byte (two codes)."""
+    p = np.array(MX_MAG_FREQ, dtype=np.float64)
+    p = np.concatenate([p, p]) / (2.0 * p.sum())          # sign bit 3, either sign
+    pb = np.outer(p, p).reshape(-1)                       # byte = hi * 16 + lo
+    edges = np.cumsum(pb) * 65536.0
+    u = np.arange(65536) + 0.5
+    byte = np.minimum(np.searchsorted(edges, u), 255)
+    return byte.astype(np.uint8)                          # index hi*16+lo is the byte value itself
+
+
+def _scale_table():
+    keys = sorted(MX_SCALE_FREQ)
+    edges = np.cumsum([MX_SCALE_FREQ[k] for k in keys]) / sum(MX_SCALE_FREQ.values()) * 65536.0
+    idx = np.minimum(np.searchsorted(edges, np.arange(65536) + 0.5), len(keys) - 1)
+    return np.array(keys, dtype=np.uint8)[idx]
+
+
+_BYTES = None
+_SCALES = None
+
+
+def mxfp4_draw(N: int, K: int, seed: int, tensor_id: int, a: int, b: int):
+    """(codes uint8 [N][K/2], scales uint8 [N][K/32]) from the (tensor_id, a, b) stream."""
+    global _BYTES, _SCALES
+    if _BYTES is None:
+        _BYTES, _SCALES = _byte_table(), _scale_table()
+    g = _rng(seed, tensor_id, a, b)
+    codes = _BYTES[g.integers(0, 65536, size=(N, K // 2), dtype=np.uint16)]
+    scales = _SCALES[g.integers(0, 65536, size=(N, K // 32), dtype=np.uint16)]
+    return codes, scales
+
+
+def make_experts_mxfp4(cfg: MoEConfig, seed: int = 0, threads: int | None = None):
+    """MXFP4 expert weights: gate_up codes [E][2I][H/2] and scales [E][2I][H/32],
+    down codes [E][H][I/2] and scales [E][H][I/32] (K-contiguous), one stream
+    per (tensor, expert).  The biases are those of make_experts."""
+    E, H, I = cfg.E, cfg.H, cfg.I
+    assert H % 32 == 0 and I % 32 == 0
+    gq = np.empty((E, 2 * I, H // 2), np.uint8)
+    gs = np.empty((E, 2 * I, H // 32), np.uint8)
+    dq = np.empty((E, H, I // 2), np.uint8)
+    ds = np.empty((E, H, I // 32), np.uint8)
+    bgu = np.empty((E, 2 * I), dtype=np.uint16)
+    bd = np.empty((E, H), dtype=np.uint16)
+
+    def one(e):
+        gq[e], gs[e] = mxfp4_draw(2 * I, H, seed, MXGU_ID, E, e)
+        dq[e], ds[e] = mxfp4_draw(H, I, seed, MXD_ID, E, e)
+        bgu[e] = normal_bf16((2 * I,), BIAS_STD, seed, BGU_ID, E, e)
+        bd[e] = normal_bf16((H,), BIAS_STD, seed, BD_ID, E, e)
+
+    if threads is None:
+        threads = min(16, max(1, len(_affinity())))
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(one, range(E)))
+    return gq, gs, bgu, dq, ds, bd

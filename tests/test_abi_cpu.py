@@ -143,3 +143,31 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mod.library(str(tmp_path / "missing.so"))
     finally:
         mod._lib = saved
+
+
+def _fwd_mx(lib, T=8, H=64, E=8, k=2, I=64, ptrs=None, ws_bytes=1 << 30):
+    p = [FAKE] * 10 if ptrs is None else ptrs
+    vp = [ctypes.c_void_p(v) if v else None for v in p]
+    return lib.moe_forward_mxfp4(*vp[:9], T, H, E, k, I, vp[9], None, None, ctypes.c_void_p(FAKE), ws_bytes, None)
+
+
+def test_mxfp4_calls_validate(lib):
+    v = ctypes.c_void_p(FAKE)
+    # H and I must be multiples of 32 (one scale per 32 values along K)
+    assert _fwd_mx(lib, H=40) == INVALID and b"multiples of 32" in lib.moe_last_error()
+    assert _fwd_mx(lib, I=48) == INVALID
+    for i in range(10):
+        p = [FAKE] * 10
+        p[i] = 0
+        assert _fwd_mx(lib, ptrs=p) == INVALID
+        assert b"is NULL" in lib.moe_last_error()
+    assert _fwd_mx(lib, ws_bytes=16) == WORKSPACE
+    assert _fwd_mx(lib, T=0) == OK
+    assert lib.moe_gate_up_mxfp4(v, v, v, v, v, v, v, 4, 72, 8, 2, 64, v, None) == INVALID
+    assert lib.moe_down_mxfp4(v, v, None, v, v, v, 4, 64, 8, 2, 64, v, None) == INVALID
+    # the quantiser: K % 32 == 0, N % 8 == 0, codes 16-byte aligned
+    assert lib.moe_quantize_mxfp4(v, 4, 40, 64, v, v, None) == INVALID and b"K=40" in lib.moe_last_error()
+    assert lib.moe_quantize_mxfp4(v, 4, 64, 12, v, v, None) == INVALID and b"N=12" in lib.moe_last_error()
+    assert lib.moe_quantize_mxfp4(v, 0, 64, 64, v, v, None) == INVALID
+    assert lib.moe_quantize_mxfp4(v, 4, 64, 64, ctypes.c_void_p(FAKE + 8), v, None) == INVALID
+    assert b"aligned" in lib.moe_last_error()
