@@ -51,6 +51,22 @@ def _alg_bytes_gate_up(cfg, D):
     return D * (H * 2 * I * 2 + 2 * I * 2) + T * H * 2 + T * k * I * 2
 
 
+def _mx_bytes(K, N):
+    """One MXFP4 weight [N][K]: 4-bit codes plus one scale byte per 32 values."""
+    return N * K // 2 + N * K // 32
+
+
+def _alg_bytes_layer_mxfp4(cfg, D):
+    H, I, E, T = cfg.H, cfg.I, cfg.E, cfg.T
+    per_expert = _mx_bytes(H, 2 * I) + _mx_bytes(I, H) + 2 * I * 2 + H * 2
+    return D * per_expert + E * H * 2 + E * 2 + 2 * T * H * 2
+
+
+def _alg_bytes_gate_up_mxfp4(cfg, D):
+    H, I, T, k = cfg.H, cfg.I, cfg.T, cfg.k
+    return D * (_mx_bytes(H, 2 * I) + 2 * I * 2) + T * H * 2 + T * k * I * 2
+
+
 def _alg_flops_layer(cfg):
     H, I, E, T, k = cfg.H, cfg.I, cfg.E, cfg.T, cfg.k
     return T * (2 * H * E + k * (2 * H * 2 * I + 2 * I * H))
@@ -83,9 +99,10 @@ def _traffic(kernel_file, workload, launches_bytes_unit=1.0):
         return None
 
 
-def cpu_baseline(inp, k, min_seconds=10.0, max_reps=3):
+def cpu_baseline(inp, k, min_seconds=10.0, max_reps=3, mx_arrays=None):
     """The float64 oracle on the host cores over the whole workload, repeated
-    until about min_seconds of CPU time (at most max_reps runs)."""
+    until about min_seconds of CPU time (at most max_reps runs).  mx_arrays:
+    the MXFP4 inputs, timed through the oracle's MXFP4 forward instead."""
     import numpy as np
     import oracle.moe_oracle as orc
     try:
@@ -97,11 +114,15 @@ def cpu_baseline(inp, k, min_seconds=10.0, max_reps=3):
     t_all = time.perf_counter()
     while len(times) < max_reps and (time.perf_counter() - t_all) < min_seconds:
         t0 = time.perf_counter()
-        orc.moe_forward(*inp.arrays(), k=k)
+        if mx_arrays is None:
+            orc.moe_forward(*inp.arrays(), k=k)
+        else:
+            orc.moe_forward_mxfp4(*mx_arrays, k=k)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     return {"value": inp.cfg.T / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"whole {inp.cfg.name} batch (T={inp.cfg.T}) through the float64 numpy oracle, "
+            "sample": f"whole {inp.cfg.name} batch (T={inp.cfg.T}) through the float64 numpy oracle"
+                      f"{' (MXFP4 weights)' if mx_arrays is not None else ''}, "
                       f"median of {len(times)} runs of {t:.2f} s"}
 
 
@@ -160,6 +181,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
+    ap.add_argument("--weights", default="bf16", choices=["bf16", "mxfp4"],
+                    help="expert weight format: bf16 (moe_forward) or MXFP4 W4A16 (moe_forward_mxfp4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ep", type=int, default=1,
                     help="also time one expert-parallel rank's share of W ranks: experts [0, E/W), "
@@ -197,6 +220,18 @@ def main(argv=None):
         print("[bench] copy probe: 1 GiB read + 1 GiB written", file=sys.stderr, flush=True)
 
     x, Wr, br, Wgu, bgu, Wd, bd = [dev(a) for a in inp.arrays()]
+    mx = args.weights == "mxfp4"
+    mx_arrays = None
+    if mx:
+        if args.ep > 1:
+            print("bench.py: --ep is measured with bf16 weights only", file=sys.stderr)
+            return 2
+        gq, gs, bgu_m, dq, ds, bd_m = d.make_experts_mxfp4(cfg, seed=0)
+        mx_arrays = (inp.x, inp.Wr, inp.br, gq, gs, bgu_m, dq, ds, bd_m)
+        Wgu_q, Wgu_s, Wd_q, Wd_s = [torch.from_numpy(a).cuda() for a in (gq, gs, dq, ds)]
+        bgu, bd = dev(bgu_m), dev(bd_m)
+        del Wgu, Wd
+        print("[bench] MXFP4 expert weights ready", file=sys.stderr, flush=True)
     T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
     ws = binding.alloc_workspace(T, H, E, k, I)
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
@@ -205,8 +240,12 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
 
     def step(st=None):
-        binding.moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k=k, y=y, workspace=ws, topk_ids=ids, topk_w=w,
-                            path=args.path, stream=st if st is not None else stream)
+        if mx:
+            binding.moe_forward_mxfp4(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k=k, y=y, workspace=ws,
+                                      topk_ids=ids, topk_w=w, stream=st if st is not None else stream)
+        else:
+            binding.moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k=k, y=y, workspace=ws, topk_ids=ids, topk_w=w,
+                                path=args.path, stream=st if st is not None else stream)
 
     for _ in range(args.warmup):
         step()
@@ -265,10 +304,16 @@ def main(argv=None):
         binding._check(st, "moe_permute")
         if ev:
             ev[0].record(stream)
-        binding.moe_gate_up(x, Wgu, bgu, cnt, off, rows, k, path=args.path, h=h, stream=stream)
+        if mx:
+            binding.moe_gate_up_mxfp4(x, Wgu_q, Wgu_s, bgu, cnt, off, rows, k, h=h, stream=stream)
+        else:
+            binding.moe_gate_up(x, Wgu, bgu, cnt, off, rows, k, path=args.path, h=h, stream=stream)
         if ev:
             ev[1].record(stream)
-        binding.moe_down(h, Wd, bd, cnt, off, T, k, path=args.path, o=o, stream=stream)
+        if mx:
+            binding.moe_down_mxfp4(h, Wd_q, Wd_s, bd, cnt, off, T, k, o=o, stream=stream)
+        else:
+            binding.moe_down(h, Wd, bd, cnt, off, T, k, path=args.path, o=o, stream=stream)
         binding.moe_combine(o, pos, w, y=y, stream=stream)
 
     for _ in range(max(2, args.warmup // 2)):
@@ -281,11 +326,16 @@ def main(argv=None):
 
     D = int((torch.bincount(ids.reshape(-1).long(), minlength=E) > 0).sum().item())
     path = args.path if args.path != "auto" else binding.expert_path(T, E, k)
-    gu_bytes = _alg_bytes_gate_up(cfg, D)
+    if mx:
+        path = "mxfp4"
+    gu_bytes = _alg_bytes_gate_up_mxfp4(cfg, D) if mx else _alg_bytes_gate_up(cfg, D)
     gu_flops = 2 * T * k * H * 2 * I
     gu_file = f"moe_layer_route_amd/csrc/{path}.hip"
     traffic = _traffic(gu_file, cfg.name)
-    if path == "gemv":
+    if mx:
+        roofline = {"bound": "hbm", "kernel": "gemv_mxfp4_kernel<gate_up>",
+                    "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    elif path == "gemv":
         roofline = {"bound": "hbm", "kernel": "gemv_expert_kernel<gate_up>",
                     "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
@@ -294,7 +344,7 @@ def main(argv=None):
                     "unit": "TFLOP/s"}
     roofline.update(frac=roofline["achieved"] / roofline["peak"], traffic=traffic,
                     alg_bytes_per_launch=gu_bytes, alg_flops_per_launch=gu_flops, launch_us=gate_up_ms * 1e3)
-    layer_bytes = _alg_bytes_layer(cfg, D)
+    layer_bytes = _alg_bytes_layer_mxfp4(cfg, D) if mx else _alg_bytes_layer(cfg, D)
     layer_flops = _alg_flops_layer(cfg)
     step_s = ms_per_step * 1e-3
 
@@ -342,7 +392,7 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic (seeded normal bf16 inputs of the gpt-oss MoE block shapes; random-init weights)",
         "config": {"workload": f"{cfg.name}: {cfg.description}", "T": T, "H": H, "I": I, "E": E, "k": k,
-                   "seed": 0, "path": path, "live_experts": D},
+                   "seed": 0, "path": path, "live_experts": D, "weights": args.weights},
         "roofline": roofline,
         "layer": {"alg_bytes": layer_bytes, "alg_flops": layer_flops,
                   "hbm_GBs": layer_bytes / step_s / 1e9, "hbm_frac": layer_bytes / step_s / 1e9 / HBM_PEAK_GBS,
@@ -357,7 +407,7 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp, k)
+        out["cpu_baseline"] = cpu_baseline(inp, k, mx_arrays=mx_arrays)
     print(json.dumps(out), flush=True)
     return 0
 

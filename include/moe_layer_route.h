@@ -257,9 +257,10 @@ MOE_API int moe_combine(const float* o, const int32_t* pos, const float* topk_w,
  *                              bits 4-7.  E2M1 code: bit 3 sign, bits 2-1
  *                              exponent (bias 1), bit 0 mantissa; magnitudes
  *                              0, 0.5, 1, 1.5, 2, 3, 4, 6.
- *   scales uint8 [E][N][K/32]  the 32 values k = 32b .. 32b+31 of column n are
- *                              multiplied by 2^(scales[e][n][b] - 127); 255 is
- *                              NaN.
+ *   scales uint8 [E][K/32][N]  the 32 values k = 32b .. 32b+31 of column n are
+ *                              multiplied by 2^(scales[e][b][n] - 127); 255 is
+ *                              NaN (block-major: the scales of one block of
+ *                              all columns are contiguous).
  * The weight value is E2M1(code) * 2^(scale - 127), exactly.  Requires
  * H % 32 == 0 and I % 32 == 0; codes and scales 16-byte aligned.
  */
@@ -274,16 +275,16 @@ MOE_API int moe_combine(const float* o, const int32_t* pos, const float* topk_w,
  * reference conversion.)  K % 32 == 0, N % 8 == 0.
  *   W       bf16 [E][K][N]   in
  *   codes   uint8 [E][N][K/2]   out
- *   scales  uint8 [E][N][K/32]  out
+ *   scales  uint8 [E][K/32][N]  out
  */
 MOE_API int moe_quantize_mxfp4(const void* W, int32_t E, int32_t K, int32_t N, void* codes, void* scales,
                                void* stream);
 
 /*
  * moe_forward_mxfp4 -- moe_forward with MXFP4 expert weights:
- *   Wgu_q uint8 [E][2I][H/2], Wgu_s uint8 [E][2I][H/32]   gate_up (columns
+ *   Wgu_q uint8 [E][2I][H/2], Wgu_s uint8 [E][H/32][2I]   gate_up (columns
  *                          interleaved gate0, up0, gate1, ... as in moe_forward)
- *   Wd_q  uint8 [E][H][I/2],  Wd_s  uint8 [E][H][I/32]    down
+ *   Wd_q  uint8 [E][H][I/2],  Wd_s  uint8 [E][I/32][H]    down
  * Every other argument, the workspace size (moe_workspace_bytes) and the
  * result's definition are those of moe_forward with the weights replaced by
  * their exact dequantised values; the dequantised weights are bf16 operands

@@ -249,7 +249,7 @@ def moe_combine(o, pos, topk_w, y=None, stream=None):
 
 
 # ---------------------------------------------------------------------------
-# MXFP4 expert weights: codes uint8 [E][N][K/2] and scales uint8 [E][N][K/32]
+# MXFP4 expert weights: codes uint8 [E][N][K/2] and scales uint8 [E][K/32][N]
 # (gate_up: K = H, N = 2I; down: K = I, N = H)
 # ---------------------------------------------------------------------------
 def _u8(*ts):
@@ -259,14 +259,14 @@ def _u8(*ts):
 
 
 def moe_quantize_mxfp4(W, codes=None, scales=None, stream=None):
-    """bf16 weights [E][K][N] (x.W form) -> (codes uint8 [E][N][K/2], scales uint8 [E][N][K/32])."""
+    """bf16 weights [E][K][N] (x.W form) -> (codes uint8 [E][N][K/2], scales uint8 [E][K/32][N])."""
     _dev(W)
     _b16(W)
     E, K, N = W.shape
     if codes is None:
         codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=W.device)
     if scales is None:
-        scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device=W.device)
+        scales = torch.empty((E, K // 32, N), dtype=torch.uint8, device=W.device)
     _dev(codes, scales)
     _u8(codes, scales)
     _check(library().moe_quantize_mxfp4(_ptr(W), E, K, N, _ptr(codes), _ptr(scales), _stream(stream)),

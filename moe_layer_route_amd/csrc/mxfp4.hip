@@ -11,8 +11,8 @@
 // Layout (K = contraction dimension, N = output columns):
 //   codes  uint8 [E][N][K/2]: row n holds the K values of column n, two per
 //          byte, k = 2i in bits 0-3 and k = 2i+1 in bits 4-7;
-//   scales uint8 [E][N][K/32]: 2^(s - 127) for the 32 values k = 32b..32b+31
-//          of column n (s = 255 is NaN).
+//   scales uint8 [E][K/32][N]: scales[e][b][n] = s gives 2^(s - 127) for the
+//          32 values k = 32b..32b+31 of column n (s = 255 is NaN).
 // E2M1 code: bit 3 sign, bits 2-1 exponent (bias 1), bit 0 mantissa; the
 // magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.
 #include "device_common.h"
@@ -86,27 +86,28 @@ __global__ __launch_bounds__(kQThreads) void mxfp4_quantize_kernel(const bf16_t*
   const size_t row = (size_t)e * N + n;
   *reinterpret_cast<u32x4_t*>(codes + row * (K / 2) + 16 * (size_t)b) =
       u32x4_t{packed[0], packed[1], packed[2], packed[3]};
-  scales[row * (K / 32) + b] = (uint8_t)sbyte;
+  scales[((size_t)e * (K / 32) + b) * N + n] = (uint8_t)sbyte;
 }
 
 // ---------------------------------------------------------------------------
-// Weight-streaming expert kernel.  A workgroup owns one expert and a slice of
-// 128 output columns; its four waves split K in quads of four 32-value
-// blocks (128 K).  Lane (g = lane/16, c = lane%16), call j = 0..7, reads
-// block 4q+g of column n0+8c+j: 16 bytes, the whole block.  The four 8-value
-// quarters t of that block are the B operands of four
-// v_mfma_f32_16x16x32_bf16 calls, K index 32(4q+g) + 8t + i in MFMA K slot
-// (g, i); the token operand is loaded in the same order (lane (row, g), 16
-// bytes of x at K = 32(4q+g) + 8t).  MFMA column c of call j is weight column
-// n0+8c+j, as in the bf16 kernel, so gate and up of one pair (j, j+1) sit in
-// the same lane.  The dequantisation is v_cvt_scalef32_pk_bf16_fp4 (two
-// codes per instruction, exact for every scale).  The slice's scales are
-// staged transposed in LDS ([block][column]), so a lane reads the scales of
-// its eight columns with one 8-byte access.
+// Weight-streaming expert kernel.  One wave per workgroup owns one expert and
+// a slice of 64 output columns over the whole of K, so its partial sums never
+// leave the registers.  K is walked in steps of four 32-value blocks (128 K).
+// Lane (g = lane/16, c = lane%16), call j = 0..3, reads block 4q+g of column
+// n0+4c+j: 16 bytes, the whole block.  The four 8-value quarters t of that
+// block are the B operands of four v_mfma_f32_16x16x32_bf16 calls, K index
+// 32(4q+g) + 8t + i in MFMA K slot (g, i); the token operand is loaded in the
+// same order (lane (row, g), 16 bytes of x at K = 32(4q+g) + 8t).  MFMA
+// column c of call j is weight column n0+4c+j, so gate and up of one pair
+// (calls j, j+1) sit in the same lane.  The scales of the lane's four columns
+// for its block are one 4-byte load (scales are block-major).  The
+// dequantisation is v_cvt_scalef32_pk_bf16_fp4 (two codes per instruction,
+// exact for every scale).  The weight loads run three steps ahead in a ring
+// of four register sets (the bytes in flight are what the streaming rate
+// depends on); the token rows come from L2 and run one step ahead.
 // ---------------------------------------------------------------------------
-constexpr int kMxThreads = 256;
-constexpr int kMxWaves = 4;
-constexpr int kMxCols = 128;
+constexpr int kMxNJ = 4;                 // columns per lane (calls j)
+constexpr int kMxCols = 16 * kMxNJ;      // 64 columns per workgroup
 constexpr int64_t kMxOneChunkMeanRows = 10;
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
@@ -129,66 +130,48 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t w, float s) {
                  __builtin_bit_cast(uint32_t, d)};
 }
 
+struct MxW {
+  u32x4_t w[kMxNJ];   // block 4q+g of the lane's columns
+  uint32_t s;         // their four scale bytes
+};
+template <int MG>
+struct MxA {
+  u32x4_t a[MG][4];   // token rows: 16 bytes at K = 32(4q+g) + 8t
+};
+
 template <bool GATE_UP, int MG>
-__global__ __launch_bounds__(kMxThreads) void gemv_mxfp4_kernel(
+__global__ __launch_bounds__(kWave) void gemv_mxfp4_kernel(
     const bf16_t* __restrict__ A,        // gate_up: x [T][K]; down: h [S][K] in permuted order
     const uint8_t* __restrict__ Wq,      // [E][N][K/2]
-    const uint8_t* __restrict__ Ws,      // [E][N][K/32]
+    const uint8_t* __restrict__ Ws,      // [E][K/32][N]
     const bf16_t* __restrict__ bias,     // [E][N]
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ off,
     const int32_t* __restrict__ rows,    // gate_up only: permuted slot ids
     int K, int N, int kslots, int a_rows, void* __restrict__ out) {
-  __shared__ float red[kMxWaves][8][4][kWave];   // 32 KB: one chunk's partial sums per wave
-  extern __shared__ __align__(16) uint8_t sc[];  // [K/32][128] scales of the slice
-
   const int e = blockIdx.y;
   const int M = cnt[e];
-  if (M == 0) return;   // block-uniform: no load, no barrier for an expert without rows
+  if (M == 0) return;   // the whole (one-wave) workgroup: no load for an expert without rows
   const int row0 = off[e];
   const int nblk = K / 32;
-  const int n0 = blockIdx.x * kMxCols;
-  const int ncols = min(kMxCols, N - n0);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = threadIdx.x;
   const int g = lane >> 4;
   const int c = lane & 15;
-
-  // ---- scales of the slice -> LDS [block][column] ----
-  {
-    const uint32_t bytes = (uint32_t)ncols * nblk;   // contiguous: rows n0.. of [N][K/32]
-    const rsrc_t s_rs = make_rsrc(Ws + ((size_t)e * N + n0) * nblk, bytes);
-    // 8-byte pieces: the region starts at a multiple of 8 bytes (N % 8 == 0)
-    for (uint32_t p0 = 8u * tid; p0 < bytes; p0 += 8u * kMxThreads) {
-      const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(s_rs, (int)p0, 0, 0));
-      uint32_t col = p0 / nblk, blk = p0 - col * nblk;   // walked forward byte by byte
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (p0 + q < bytes) sc[blk * kMxCols + col] = (uint8_t)(v[q / 4] >> (8 * (q % 4)));
-        ++blk;
-        const bool wrap = blk == (uint32_t)nblk;
-        blk = wrap ? 0u : blk;
-        col += wrap ? 1u : 0u;
-      }
-    }
-  }
-  __syncthreads();
+  // N % 8 == 0 and ncol % 4 == 0: a lane's four columns are all in range or all out
+  const int ncol = blockIdx.x * kMxCols + kMxNJ * c;
+  const bool col_ok = ncol < N;
 
   const uint32_t row_bytes = (uint32_t)K / 2;
   const rsrc_t w_rs = make_rsrc(Wq + (size_t)e * N * row_bytes, (uint32_t)N * row_bytes);
+  const rsrc_t s_rs = make_rsrc(Ws + (size_t)e * nblk * N, (uint32_t)(nblk * N));
   const rsrc_t a_rs = make_rsrc(A, (uint32_t)((size_t)a_rows * K * 2));
-  uint32_t w_off[8];
+  uint32_t w_off[kMxNJ];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) w_off[j] = (uint32_t)min(n0 + 8 * c + j, N - 1) * row_bytes;
-  const bool col_ok = n0 + 8 * c < N;
-
+  for (int j = 0; j < kMxNJ; ++j) w_off[j] = (uint32_t)min(ncol + j, N - 1) * row_bytes;
+  const uint32_t s_col = (uint32_t)min(ncol, N - kMxNJ);
   const int nq = (nblk + 3) / 4;
-  const int q_begin = (nq * wave) / kMxWaves;
-  const int q_end = (nq * (wave + 1)) / kMxWaves;
 
   for (int r0 = 0; r0 < M; r0 += 16 * MG) {
-    const int nch = min(MG, (M - r0 + 15) / 16);   // block-uniform
+    const int nch = min(MG, (M - r0 + 15) / 16);   // uniform
     uint32_t a_off[MG];
 #pragma unroll
     for (int qq = 0; qq < MG; ++qq) {
@@ -196,95 +179,112 @@ __global__ __launch_bounds__(kMxThreads) void gemv_mxfp4_kernel(
       const uint32_t r = GATE_UP ? (uint32_t)(rows[row0 + m] / kslots) : (uint32_t)(row0 + m);
       a_off[qq] = r * (uint32_t)K * 2u;
     }
-
-    f32x4_t acc[MG][8];
+    f32x4_t acc[MG][kMxNJ];
 #pragma unroll
     for (int qq = 0; qq < MG; ++qq)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[qq][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < kMxNJ; ++j) acc[qq][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Loads of quad q into one register set: the lane's block 4q+g of its
-    // eight columns and the 4 x MG pieces of token rows.  A block past K (or
-    // a quad past this wave's range) is sent outside the descriptors.
-    auto load = [&](int q, u32x4_t (&wd)[8], u32x4_t (&ad)[MG][4]) {
+    // loads of step q; a block past K reads 0 (sent outside the descriptors)
+    auto load_w = [&](int q, MxW& d) {
       const int b = 4 * q + g;
-      const bool in = q < q_end && b < nblk;
+      const bool in = b < nblk;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) wd[j] = buf_ld16_nt(w_rs, in ? w_off[j] + 16u * b : kOutOfRange);
+      for (int j = 0; j < kMxNJ; ++j) d.w[j] = buf_ld16(w_rs, in ? w_off[j] + 16u * b : kOutOfRange);
+      d.s = __builtin_amdgcn_raw_buffer_load_b32(s_rs, (int)(in ? (uint32_t)b * N + s_col : kOutOfRange), 0, 0);
+    };
+    auto load_a = [&](int q, MxA<MG>& d) {
+      const int b = 4 * q + g;
+      const bool in = b < nblk;
 #pragma unroll
       for (int qq = 0; qq < MG; ++qq)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          ad[qq][t] = buf_ld16(a_rs, in ? a_off[qq] + (uint32_t)(32 * b + 8 * t) * 2u : kOutOfRange);
+          d.a[qq][t] = buf_ld16(a_rs, in ? a_off[qq] + (uint32_t)(32 * b + 8 * t) * 2u : kOutOfRange);
     };
-    auto step = [&](int q, const u32x4_t (&wd)[8], const u32x4_t (&ad)[MG][4]) {
-      const int b = min(4 * q + g, nblk - 1);
-      const uint2 s8 = *reinterpret_cast<const uint2*>(sc + b * kMxCols + 8 * c);
-      float s[8];
+    auto step = [&](const MxW& dw, const MxA<MG>& da) {
+      float sc[kMxNJ];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s[j] = ue8m0_to_f32(((j < 4 ? s8.x : s8.y) >> (8 * (j & 3))) & 0xFF);
+      for (int j = 0; j < kMxNJ; ++j) sc[j] = ue8m0_to_f32((dw.s >> (8 * j)) & 0xFF);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const u32x4_t bw = dequant8(wd[j][t], s[j]);
-          acc[0][j] = mfma16x16x32(ad[0][t], bw, acc[0][j]);
+        for (int j = 0; j < kMxNJ; ++j) {
+          const u32x4_t bw = dequant8(dw.w[j][t], sc[j]);
+          acc[0][j] = mfma16x16x32(da.a[0][t], bw, acc[0][j]);
           if (MG > 1 && nch > 1) {
 #pragma unroll
-            for (int qq = 1; qq < MG; ++qq) acc[qq][j] = mfma16x16x32(ad[qq][t], bw, acc[qq][j]);
+            for (int qq = 1; qq < MG; ++qq) acc[qq][j] = mfma16x16x32(da.a[qq][t], bw, acc[qq][j]);
           }
         }
     };
 
-    u32x4_t wcur[8], wnxt[8], acur[MG][4], anxt[MG][4];
-    load(q_begin, wcur, acur);
-    int q = q_begin;
-    for (; q + 2 <= q_end; q += 2) {
-      load(q + 1, wnxt, anxt);
-      step(q, wcur, acur);
-      load(q + 2, wcur, acur);
-      step(q + 1, wnxt, anxt);
+    MxW w0, w1, w2, w3;
+    MxA<MG> a0, a1;
+    load_w(0, w0);
+    load_w(1, w1);
+    load_w(2, w2);
+    load_a(0, a0);
+    int q = 0;
+    for (; q + 4 <= nq; q += 4) {
+      load_w(q + 3, w3);
+      load_a(q + 1, a1);
+      step(w0, a0);
+      load_w(q + 4, w0);
+      load_a(q + 2, a0);
+      step(w1, a1);
+      load_w(q + 5, w1);
+      load_a(q + 3, a1);
+      step(w2, a0);
+      load_w(q + 6, w2);
+      load_a(q + 4, a0);
+      step(w3, a1);
     }
-    if (q < q_end) step(q, wcur, acur);
+    // 0..3 steps left; w0, w1, w2 hold steps q, q+1, q+2 and a0 holds step q
+    if (q < nq) {
+      load_a(q + 1, a1);
+      step(w0, a0);
+    }
+    if (q + 1 < nq) {
+      load_a(q + 2, a0);
+      step(w1, a1);
+    }
+    if (q + 2 < nq) step(w2, a0);
 
-    // Sum the four K partials (fixed order: wave 0, 1, 2, 3), then the epilogue.
-    // Wave w finishes MFMA calls j = 2w and 2w+1 (columns n0+8c+2w, +2w+1).
+    // epilogue: 16x16 accumulator layout, lane (c, g) element v holds row
+    // 4g + v of MFMA column c = weight column ncol + j of call j
+    if (col_ok) {
+      float bb[kMxNJ];
+      {
+        // two 4-byte reads: the bias is only guaranteed 4-byte alignment
+        const uint32_t* bp = reinterpret_cast<const uint32_t*>(bias + (size_t)e * N + ncol);
+        const uint32_t b01 = bp[0], b23 = bp[1];
+        bb[0] = bf16lo(b01);
+        bb[1] = bf16hi(b01);
+        bb[2] = bf16lo(b23);
+        bb[3] = bf16hi(b23);
+      }
 #pragma unroll
-    for (int qq = 0; qq < MG; ++qq) {
-      if (qq < nch) {
+      for (int qq = 0; qq < MG; ++qq) {
+        if (qq < nch) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[qq][j][v];
-        __syncthreads();
-        const int col = n0 + 8 * c + 2 * wave;
-        float b0 = 0.f, b1 = 0.f;
-        if (col_ok) {
-          const uint32_t bw = *reinterpret_cast<const uint32_t*>(bias + (size_t)e * N + col);
-          b0 = bf16lo(bw);
-          b1 = bf16hi(bw);
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int m = r0 + 16 * qq + 4 * g + v;   // C row held in slot v of this lane
-          float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-          for (int w2 = 0; w2 < kMxWaves; ++w2) {
-            s0 += red[w2][2 * wave][v][lane];
-            s1 += red[w2][2 * wave + 1][v][lane];
-          }
-          if (m < M && col_ok) {
-            const size_t orow = (size_t)(row0 + m);
-            if (GATE_UP) {
-              const float hv = clamped_glu(s0 + b0, s1 + b1);
-              reinterpret_cast<uint16_t*>(out)[orow * (N / 2) + col / 2] = (uint16_t)f32_to_bf16(hv);
-            } else {
-              *reinterpret_cast<float2*>(reinterpret_cast<float*>(out) + orow * N + col) =
-                  make_float2(s0 + b0, s1 + b1);
+          for (int v = 0; v < 4; ++v) {
+            const int m = r0 + 16 * qq + 4 * g + v;
+            if (m < M) {
+              const size_t orow = (size_t)(row0 + m);
+              if (GATE_UP) {
+                const float h0 = clamped_glu(acc[qq][0][v] + bb[0], acc[qq][1][v] + bb[1]);
+                const float h1 = clamped_glu(acc[qq][2][v] + bb[2], acc[qq][3][v] + bb[3]);
+                *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + orow * (N / 2) + ncol / 2) =
+                    pack_bf16x2(h0, h1);
+              } else {
+                *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + orow * N + ncol) =
+                    f32x4_t{acc[qq][0][v] + bb[0], acc[qq][1][v] + bb[1], acc[qq][2][v] + bb[2],
+                            acc[qq][3][v] + bb[3]};
+              }
             }
           }
         }
-        __syncthreads();
       }
     }
   }
@@ -298,12 +298,10 @@ hipError_t launch_mx(const void* A, const void* Wq, const void* Ws, const void* 
   // 2 GiB, so an offset at kOutOfRange never wraps back into range
   if (a_rows * K * 2 >= ((int64_t)1 << 31) || (int64_t)N * K / 2 >= ((int64_t)1 << 31)) return hipErrorNotSupported;
   dim3 grid((unsigned)((N + kMxCols - 1) / kMxCols), (unsigned)E);
-  const size_t lds = (size_t)(K / 32) * kMxCols;
   const bool one = T * k <= kMxOneChunkMeanRows * E;
   auto kern = one ? gemv_mxfp4_kernel<GATE_UP, 1> : gemv_mxfp4_kernel<GATE_UP, 2>;
-  hipLaunchKernelGGL(kern, grid, dim3(kMxThreads), lds, stream, (const bf16_t*)A, (const uint8_t*)Wq,
-                     (const uint8_t*)Ws, (const bf16_t*)bias, cnt, off, rows, K, N, GATE_UP ? k : 1, (int)a_rows,
-                     out);
+  hipLaunchKernelGGL(kern, grid, dim3(kWave), 0, stream, (const bf16_t*)A, (const uint8_t*)Wq, (const uint8_t*)Ws,
+                     (const bf16_t*)bias, cnt, off, rows, K, N, GATE_UP ? k : 1, (int)a_rows, out);
   return hipGetLastError();
 }
 

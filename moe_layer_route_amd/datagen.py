@@ -238,26 +238,27 @@ _SCALES = None
 
 
 def mxfp4_draw(N: int, K: int, seed: int, tensor_id: int, a: int, b: int):
-    """(codes uint8 [N][K/2], scales uint8 [N][K/32]) from the (tensor_id, a, b) stream."""
+    """(codes uint8 [N][K/2], scales uint8 [K/32][N]) from the (tensor_id, a, b) stream."""
     global _BYTES, _SCALES
     if _BYTES is None:
         _BYTES, _SCALES = _byte_table(), _scale_table()
     g = _rng(seed, tensor_id, a, b)
     codes = _BYTES[g.integers(0, 65536, size=(N, K // 2), dtype=np.uint16)]
-    scales = _SCALES[g.integers(0, 65536, size=(N, K // 32), dtype=np.uint16)]
+    scales = _SCALES[g.integers(0, 65536, size=(K // 32, N), dtype=np.uint16)]
     return codes, scales
 
 
 def make_experts_mxfp4(cfg: MoEConfig, seed: int = 0, threads: int | None = None):
-    """MXFP4 expert weights: gate_up codes [E][2I][H/2] and scales [E][2I][H/32],
-    down codes [E][H][I/2] and scales [E][H][I/32] (K-contiguous), one stream
-    per (tensor, expert).  The biases are those of make_experts."""
+    """MXFP4 expert weights: gate_up codes [E][2I][H/2] and scales [E][H/32][2I],
+    down codes [E][H][I/2] and scales [E][I/32][H] (codes K-contiguous, scales
+    block-major), one stream per (tensor, expert).  The biases are those of
+    make_experts."""
     E, H, I = cfg.E, cfg.H, cfg.I
     assert H % 32 == 0 and I % 32 == 0
     gq = np.empty((E, 2 * I, H // 2), np.uint8)
-    gs = np.empty((E, 2 * I, H // 32), np.uint8)
+    gs = np.empty((E, H // 32, 2 * I), np.uint8)
     dq = np.empty((E, H, I // 2), np.uint8)
-    ds = np.empty((E, H, I // 32), np.uint8)
+    ds = np.empty((E, I // 32, H), np.uint8)
     bgu = np.empty((E, 2 * I), dtype=np.uint16)
     bd = np.empty((E, H), dtype=np.uint16)
 

@@ -196,9 +196,11 @@ def _forward(x, Wr, br, weights, I2, Hout, k, tokens=None, keep=False, experts=N
 # weights are 4-bit E2M1 values with one UE8M0 power-of-two scale per 32
 # values; activations stay bf16).  Readings (listed in the design doc):
 #   M1  a block is 32 consecutive values along the contraction dimension K
-#       (the dimension a dot product runs over), so the weights are stored
+#       (the dimension a dot product runs over), so the codes are stored
 #       K-contiguous: codes [E][N][K/2] (byte i of row n holds k = 2i in bits
-#       0-3 and k = 2i+1 in bits 4-7), scales [E][N][K/32];
+#       0-3 and k = 2i+1 in bits 4-7); the scales are stored block-major,
+#       scales [E][K/32][N] (scales[e][b][n] scales k = 32b..32b+31 of
+#       column n);
 #   M2  the quantiser is the microscaling formats' reference conversion: per
 #       block, X = 2^(floor(log2(max|v|)) - 2) (2 is the largest exponent of
 #       E2M1, whose largest value is 6 = 1.5 * 2^2), each v / X rounded to the
@@ -232,17 +234,17 @@ def ue8m0_decode(e) -> np.ndarray:
 
 
 def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """codes uint8 [..., N, K/2] and scales uint8 [..., N, K/32] -> float64 [..., N, K]."""
+    """codes uint8 [..., N, K/2] and scales uint8 [..., K/32, N] -> float64 [..., N, K]."""
     codes = np.asarray(codes, dtype=np.uint8)
     q = np.empty(codes.shape[:-1] + (2 * codes.shape[-1],), dtype=np.float64)
     q[..., 0::2] = E2M1_VALUES[codes & 15]
     q[..., 1::2] = E2M1_VALUES[codes >> 4]
-    sc = np.repeat(ue8m0_decode(scales), 32, axis=-1)
+    sc = np.repeat(np.swapaxes(ue8m0_decode(scales), -1, -2), 32, axis=-1)
     return q * sc
 
 
 def mxfp4_quantize(w: np.ndarray):
-    """float [..., N, K] (K % 32 == 0) -> (codes uint8 [..., N, K/2], scales uint8 [..., N, K/32])."""
+    """float [..., N, K] (K % 32 == 0) -> (codes uint8 [..., N, K/2], scales uint8 [..., K/32, N])."""
     w = np.asarray(w, dtype=np.float64)
     K = w.shape[-1]
     assert K % 32 == 0
@@ -264,14 +266,14 @@ def mxfp4_quantize(w: np.ndarray):
     code = (sign << 3) | mag_code
     code = code.reshape(w.shape)
     packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
-    scales = (shared + 127).astype(np.uint8)
+    scales = np.swapaxes((shared + 127).astype(np.uint8), -1, -2).copy()
     return packed, scales
 
 
 def moe_forward_mxfp4(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k: int, tokens=None, keep=False,
                       experts=None):
     """The forward with MXFP4 expert weights (W4A16): gate_up codes [E][2I][H/2]
-    and scales [E][2I][H/32], down codes [E][H][I/2] and scales [E][H][I/32];
+    and scales [E][H/32][2I], down codes [E][H][I/2] and scales [E][I/32][H];
     the weights are dequantised exactly and the rest is moe_forward."""
     def weights(e):
         return (mxfp4_dequantize(Wgu_q[e], Wgu_s[e]).T, widen(bgu[e]),

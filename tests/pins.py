@@ -377,12 +377,12 @@ def pin_ue8m0(orc):
 def pin_mxfp4_layout(orc):
     """Low nibble = even k, high nibble = odd k; one scale per 32 consecutive k."""
     codes = np.zeros((2, 32), np.uint8)          # N = 2 rows of K = 64
-    scales = np.full((2, 2), 127, np.uint8)
+    scales = np.full((2, 2), 127, np.uint8)      # [K/32][N]
     codes[0, 0] = 0x21                           # k0: code 1 (0.5), k1: code 2 (1.0)
     codes[0, 16] = 0xF7                          # k32: code 7 (6), k33: code 15 (-6)
     codes[1, 15] = 0x9C                          # k30: code 12 (-2), k31: code 9 (-0.5)
-    scales[0, 1] = 125                           # block 1 of row 0 scaled by 1/4
-    scales[1, 0] = 130                           # block 0 of row 1 scaled by 8
+    scales[1, 0] = 125                           # block 1 of row 0 scaled by 1/4
+    scales[0, 1] = 130                           # block 0 of row 1 scaled by 8
     d = orc.mxfp4_dequantize(codes, scales)
     assert d.shape == (2, 64)
     assert (d[0, 0], d[0, 1], d[0, 32], d[0, 33]) == (0.5, 1.0, 1.5, -1.5), d[0, [0, 1, 32, 33]]
@@ -438,7 +438,7 @@ def pin_mxfp4_nearest(orc):
                 xe = -127
             else:
                 xe = max(-127, min(127, math.frexp(amax)[1] - 1 - 2))
-            assert scales[r, b] == xe + 127, (r, b, scales[r, b], xe)
+            assert scales[b, r] == xe + 127, (r, b, scales[b, r], xe)
             X = 2.0 ** xe
             for i in range(32):
                 val = float(blk[i])

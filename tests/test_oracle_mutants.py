@@ -167,7 +167,7 @@ def _dequant_scales_tiled(codes, scales):
     q = np.empty(codes.shape[:-1] + (2 * codes.shape[-1],))
     q[..., 0::2] = orc.E2M1_VALUES[codes & 15]
     q[..., 1::2] = orc.E2M1_VALUES[codes >> 4]
-    return q * np.tile(orc.ue8m0_decode(scales), 32)
+    return q * np.tile(np.swapaxes(orc.ue8m0_decode(scales), -1, -2), 32)
 
 
 def _quant_variant(ties="even", emax=2, ceil_exp=False):
@@ -191,7 +191,8 @@ def _quant_variant(ties="even", emax=2, ceil_exp=False):
         else:                                     # ties to the larger magnitude
             code = 7 - cand[..., ::-1].argmax(-1)
         code = ((np.signbit(blk).astype(np.int64) << 3) | code).reshape(w.shape)
-        return (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8), (shared + 127).astype(np.uint8)
+        return ((code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8),
+                np.swapaxes((shared + 127).astype(np.uint8), -1, -2).copy())
     return f
 
 
