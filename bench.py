@@ -242,7 +242,8 @@ def main(argv=None):
     def step(st=None):
         if mx:
             binding.moe_forward_mxfp4(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k=k, y=y, workspace=ws,
-                                      topk_ids=ids, topk_w=w, stream=st if st is not None else stream)
+                                      topk_ids=ids, topk_w=w, path=args.path,
+                                      stream=st if st is not None else stream)
         else:
             binding.moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k=k, y=y, workspace=ws, topk_ids=ids, topk_w=w,
                                 path=args.path, stream=st if st is not None else stream)
@@ -305,13 +306,13 @@ def main(argv=None):
         if ev:
             ev[0].record(stream)
         if mx:
-            binding.moe_gate_up_mxfp4(x, Wgu_q, Wgu_s, bgu, cnt, off, rows, k, h=h, stream=stream)
+            binding.moe_gate_up_mxfp4(x, Wgu_q, Wgu_s, bgu, cnt, off, rows, k, h=h, path=args.path, stream=stream)
         else:
             binding.moe_gate_up(x, Wgu, bgu, cnt, off, rows, k, path=args.path, h=h, stream=stream)
         if ev:
             ev[1].record(stream)
         if mx:
-            binding.moe_down_mxfp4(h, Wd_q, Wd_s, bd, cnt, off, T, k, o=o, stream=stream)
+            binding.moe_down_mxfp4(h, Wd_q, Wd_s, bd, cnt, off, T, k, o=o, path=args.path, stream=stream)
         else:
             binding.moe_down(h, Wd, bd, cnt, off, T, k, path=args.path, o=o, stream=stream)
         binding.moe_combine(o, pos, w, y=y, stream=stream)
@@ -326,15 +327,18 @@ def main(argv=None):
 
     D = int((torch.bincount(ids.reshape(-1).long(), minlength=E) > 0).sum().item())
     path = args.path if args.path != "auto" else binding.expert_path(T, E, k)
-    if mx:
-        path = "mxfp4"
     gu_bytes = _alg_bytes_gate_up_mxfp4(cfg, D) if mx else _alg_bytes_gate_up(cfg, D)
     gu_flops = 2 * T * k * H * 2 * I
-    gu_file = f"moe_layer_route_amd/csrc/{path}.hip"
+    gu_file = f"moe_layer_route_amd/csrc/{'mxfp4' if path == 'gemv' else 'mxfp4_gemm'}.hip" if mx else \
+        f"moe_layer_route_amd/csrc/{path}.hip"
     traffic = _traffic(gu_file, cfg.name)
-    if mx:
+    if mx and path == "gemv":
         roofline = {"bound": "hbm", "kernel": "gemv_mxfp4_kernel<gate_up>",
                     "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    elif mx:
+        roofline = {"bound": "mfma", "kernel": "gemm_mxfp4_kernel<gate_up>",
+                    "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s"}
     elif path == "gemv":
         roofline = {"bound": "hbm", "kernel": "gemv_expert_kernel<gate_up>",
                     "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}

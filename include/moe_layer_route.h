@@ -288,8 +288,10 @@ MOE_API int moe_quantize_mxfp4(const void* W, int32_t E, int32_t K, int32_t N, v
  * Every other argument, the workspace size (moe_workspace_bytes) and the
  * result's definition are those of moe_forward with the weights replaced by
  * their exact dequantised values; the dequantised weights are bf16 operands
- * of the same float32-accumulating products.  The expert kernels stream the
- * 4-bit weights (one pass over each live expert's weights per 32 rows).
+ * of the same float32-accumulating products.  Expert paths as in moe_forward:
+ * MOE_PATH_GEMV streams the 4-bit weights (one pass over each live expert's
+ * weights per 32 rows), MOE_PATH_GEMM is the LDS-tiled MFMA grouped GEMM;
+ * AUTO picks from T*k/E as moe_expert_path does.
  */
 MOE_API int moe_forward_mxfp4(const void* x, const void* Wr, const void* br,
                               const void* Wgu_q, const void* Wgu_s, const void* bgu,
@@ -298,14 +300,25 @@ MOE_API int moe_forward_mxfp4(const void* x, const void* Wr, const void* br,
                               void* y, int32_t* topk_ids_out, float* topk_w_out,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_forward_mxfp4 with the expert path forced (MOE_PATH_*); both paths give
+ * the same result within rounding.  moe_forward_mxfp4 is this with MOE_PATH_AUTO. */
+MOE_API int moe_forward_mxfp4_ex(const void* x, const void* Wr, const void* br,
+                                 const void* Wgu_q, const void* Wgu_s, const void* bgu,
+                                 const void* Wd_q, const void* Wd_s, const void* bd,
+                                 int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                                 void* y, int32_t* topk_ids_out, float* topk_w_out,
+                                 void* workspace, size_t workspace_bytes, int32_t path, void* stream);
+
 /* Stage calls of moe_forward_mxfp4: moe_gate_up and moe_down with MXFP4
- * weights (same inputs, outputs and layouts otherwise). */
+ * weights (same inputs, outputs, layouts and path argument otherwise). */
 MOE_API int moe_gate_up_mxfp4(const void* x, const void* Wgu_q, const void* Wgu_s, const void* bgu,
                               const int32_t* cnt, const int32_t* off, const int32_t* rows,
-                              int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, void* h, void* stream);
+                              int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, void* h,
+                              int32_t path, void* stream);
 MOE_API int moe_down_mxfp4(const void* h, const void* Wd_q, const void* Wd_s, const void* bd,
                            const int32_t* cnt, const int32_t* off,
-                           int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, float* o, void* stream);
+                           int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, float* o,
+                           int32_t path, void* stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,8 @@ LIB_PATH = os.environ.get("MOE_LAYER_ROUTE_LIB") or os.path.join(
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace_bytes", "moe_expert_path",
            "moe_route", "moe_route_ex",
            "moe_forward", "moe_forward_ex", "moe_forward_ep", "moe_permute", "moe_gate_up", "moe_down",
-           "moe_combine", "moe_quantize_mxfp4", "moe_forward_mxfp4", "moe_gate_up_mxfp4", "moe_down_mxfp4")
+           "moe_combine", "moe_quantize_mxfp4", "moe_forward_mxfp4", "moe_forward_mxfp4_ex", "moe_gate_up_mxfp4",
+           "moe_down_mxfp4")
 
 
 class MoEError(RuntimeError):
@@ -53,8 +54,9 @@ _SIGS = {
     "moe_combine": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
     "moe_quantize_mxfp4": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "moe_forward_mxfp4": (ctypes.c_int, [_vp] * 9 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _vp]),
-    "moe_gate_up_mxfp4": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32, _vp, _vp]),
-    "moe_down_mxfp4": (ctypes.c_int, [_vp] * 6 + [_i64, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "moe_forward_mxfp4_ex": (ctypes.c_int, [_vp] * 9 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _i32, _vp]),
+    "moe_gate_up_mxfp4": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
+    "moe_down_mxfp4": (ctypes.c_int, [_vp] * 6 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
 }
 
 
@@ -275,7 +277,7 @@ def moe_quantize_mxfp4(W, codes=None, scales=None, stream=None):
 
 
 def moe_forward_mxfp4(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k: int = 4, y=None, workspace=None,
-                      topk_ids=None, topk_w=None, stream=None):
+                      topk_ids=None, topk_w=None, path="auto", stream=None):
     """moe_forward with MXFP4 expert weights; returns y (bf16 [T,H])."""
     _dev(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd)
     _b16(x, Wr, br, bgu, bd)
@@ -288,15 +290,15 @@ def moe_forward_mxfp4(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k: int = 4, 
     if workspace is None:
         workspace = alloc_workspace(T, H, E, k, I, x.device)
     _dev(y, workspace, topk_ids, topk_w)
-    st = library().moe_forward_mxfp4(_ptr(x), _ptr(Wr), _ptr(br), _ptr(Wgu_q), _ptr(Wgu_s), _ptr(bgu),
-                                     _ptr(Wd_q), _ptr(Wd_s), _ptr(bd), T, H, E, k, I, _ptr(y), _ptr(topk_ids),
-                                     _ptr(topk_w), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                     _stream(stream))
+    st = library().moe_forward_mxfp4_ex(_ptr(x), _ptr(Wr), _ptr(br), _ptr(Wgu_q), _ptr(Wgu_s), _ptr(bgu),
+                                        _ptr(Wd_q), _ptr(Wd_s), _ptr(bd), T, H, E, k, I, _ptr(y), _ptr(topk_ids),
+                                        _ptr(topk_w), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        path_code(path), _stream(stream))
     _check(st, "moe_forward_mxfp4")
     return y
 
 
-def moe_gate_up_mxfp4(x, Wgu_q, Wgu_s, bgu, cnt, off, rows, k: int, h=None, stream=None):
+def moe_gate_up_mxfp4(x, Wgu_q, Wgu_s, bgu, cnt, off, rows, k: int, h=None, path="auto", stream=None):
     """MXFP4 gate_up + bias + GLU; returns h (bf16 [T*k, I], permuted order)."""
     _dev(x, Wgu_q, Wgu_s, bgu, cnt, off, rows)
     _u8(Wgu_q, Wgu_s)
@@ -306,11 +308,12 @@ def moe_gate_up_mxfp4(x, Wgu_q, Wgu_s, bgu, cnt, off, rows, k: int, h=None, stre
     if h is None:
         h = torch.empty((max(T * k, 1), I), dtype=torch.bfloat16, device=x.device)
     _check(library().moe_gate_up_mxfp4(_ptr(x), _ptr(Wgu_q), _ptr(Wgu_s), _ptr(bgu), _ptr(cnt), _ptr(off),
-                                       _ptr(rows), T, H, E, k, I, _ptr(h), _stream(stream)), "moe_gate_up_mxfp4")
+                                       _ptr(rows), T, H, E, k, I, _ptr(h), path_code(path), _stream(stream)),
+           "moe_gate_up_mxfp4")
     return h[:T * k]
 
 
-def moe_down_mxfp4(h, Wd_q, Wd_s, bd, cnt, off, T: int, k: int, o=None, stream=None):
+def moe_down_mxfp4(h, Wd_q, Wd_s, bd, cnt, off, T: int, k: int, o=None, path="auto", stream=None):
     """MXFP4 down + bias; returns o (float32 [T*k, H], permuted order)."""
     _dev(h, Wd_q, Wd_s, bd, cnt, off)
     _u8(Wd_q, Wd_s)
@@ -319,5 +322,5 @@ def moe_down_mxfp4(h, Wd_q, Wd_s, bd, cnt, off, T: int, k: int, o=None, stream=N
     if o is None:
         o = torch.empty((max(T * k, 1), H), dtype=torch.float32, device=h.device)
     _check(library().moe_down_mxfp4(_ptr(h), _ptr(Wd_q), _ptr(Wd_s), _ptr(bd), _ptr(cnt), _ptr(off), T, H, E,
-                                    k, I, _ptr(o), _stream(stream)), "moe_down_mxfp4")
+                                    k, I, _ptr(o), path_code(path), _stream(stream)), "moe_down_mxfp4")
     return o[:T * k]

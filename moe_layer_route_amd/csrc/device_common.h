@@ -76,12 +76,13 @@ __device__ __forceinline__ void transpose8x8_b16(const u32x4_t (&in)[8], u32x4_t
   }
 }
 
-// Clamped interleaved GLU of one (gate, up) pair, float32.  The logistic
-// uses the hardware exponential and reciprocal (about 1 ulp each; h is then
-// rounded to bf16).
+// Clamped interleaved GLU of one (gate, up) pair, float32.  The clamps are
+// compare-selects so that a NaN gate or up stays NaN (min/max instructions
+// would return the bound).  The logistic uses the hardware exponential and
+// reciprocal (about 1 ulp each; h is then rounded to bf16).
 __device__ __forceinline__ float clamped_glu(float gate, float up) {
-  const float g = fminf(gate, 7.0f);
-  const float u = fminf(fmaxf(up, -7.0f), 7.0f);
+  const float g = gate > 7.0f ? 7.0f : gate;
+  const float u = up > 7.0f ? 7.0f : (up < -7.0f ? -7.0f : up);
   const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * g));
   return (u + 1.0f) * (g * s);
 }

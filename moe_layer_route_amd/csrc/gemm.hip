@@ -192,8 +192,10 @@ __global__ __launch_bounds__(kGmThreads, 1) void gemm_expert_kernel(
   u32x4_t Ra0[2], Ra1[2];
   u32x4_t F[8];
 
-  // One K step kt: transpose B(kt); issue the loads of step kt+2 (B) and
-  // kt+3 (A); multiply, reading the A fragments of kt+1 from LDS as those of
+  // One K step kt: transpose B(kt); issue the loads of step kt+3 (A) and
+  // kt+2 (B) -- A first: loads retire in order, so the store of A(kt+3) at
+  // the next step then waits for A alone, and B keeps its two steps of
+  // lead; multiply, reading the A fragments of kt+1 from LDS as those of
   // kt retire; store A(kt+2) into LDS; one barrier after the fifth of the
   // eight MFMA groups.
   // LDS ring: buffer (kt+1)%3 is read during step kt and buffer (kt+2)%3
@@ -210,8 +212,8 @@ __global__ __launch_bounds__(kGmThreads, 1) void gemm_expert_kernel(
                  "v"(bt[7])
                  : "memory");
     __builtin_amdgcn_sched_barrier(0);
-    gload_b(kt + 2, rb);
     gload_a(kt + 3, ra_load);
+    gload_b(kt + 2, rb);
     const int nbuf = (kt + 1) % kGmLdsBufs;
     auto group = [&](int mi) {
 #pragma unroll
@@ -252,15 +254,15 @@ __global__ __launch_bounds__(kGmThreads, 1) void gemm_expert_kernel(
     }
   };
 
-  // Prologue: the loads in the order the steps issue them (B(j) then
-  // A(j+1)), so the wait counts of the first steps match the later ones.
+  // Prologue: the loads in the order the steps issue them (A(j+1) then
+  // B(j)), so the wait counts of the first steps match the later ones.
   const int nk = (K + kGmBK - 1) / kGmBK;
   gload_a(0, Ra0);
-  gload_b(0, Rb0);
   gload_a(1, Ra1);
+  gload_b(0, Rb0);
   lstore(0, Ra0);
-  gload_b(1, Rb1);
   gload_a(2, Ra0);
+  gload_b(1, Rb1);
   lstore(1, Ra1);
   __syncthreads();
 #pragma unroll

@@ -45,6 +45,13 @@ hipError_t launch_mxfp4_down(const void* h, const void* Wq, const void* Ws, cons
                              const int32_t* off, int64_t T, int H, int E, int k, int I, float* o,
                              hipStream_t stream);
 
+hipError_t launch_gemm_mxfp4_gate_up(const void* x, const void* Wq, const void* Ws, const void* bgu,
+                                     const int32_t* cnt, const int32_t* off, const int32_t* rows, int64_t T, int H,
+                                     int E, int k, int I, void* h, hipStream_t stream);
+hipError_t launch_gemm_mxfp4_down(const void* h, const void* Wq, const void* Ws, const void* bd, const int32_t* cnt,
+                                  const int32_t* off, int64_t T, int H, int E, int k, int I, float* o,
+                                  hipStream_t stream);
+
 // slots with pos < 0 are left out; out_f32: y is float32 (partial sums), else bf16
 hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, int64_t T, int H, int k,
                           void* y, hipStream_t stream, bool out_f32 = false);

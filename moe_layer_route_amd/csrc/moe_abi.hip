@@ -346,10 +346,32 @@ int moe_quantize_mxfp4(const void* W, int32_t E, int32_t K, int32_t N, void* cod
   return ok();
 }
 
-int moe_forward_mxfp4(const void* x, const void* Wr, const void* br, const void* Wgu_q, const void* Wgu_s,
-                      const void* bgu, const void* Wd_q, const void* Wd_s, const void* bd, int64_t T, int32_t H,
-                      int32_t E, int32_t k, int32_t I, void* y, int32_t* topk_ids_out, float* topk_w_out,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+static int run_gate_up_mx(const char* fn, const void* x, const void* Wq, const void* Ws, const void* bgu,
+                          const int32_t* cnt, const int32_t* off, const int32_t* rows, int64_t T, int32_t H, int32_t E,
+                          int32_t k, int32_t I, void* h, int32_t path, hipStream_t s) {
+  path = choose_path(path, T, E, k);
+  if (path == MOE_PATH_GEMV)
+    return hip_status(fn, moe::launch_mxfp4_gate_up(x, Wq, Ws, bgu, cnt, off, rows, T, H, E, k, I, h, s));
+  if (path == MOE_PATH_GEMM)
+    return hip_status(fn, moe::launch_gemm_mxfp4_gate_up(x, Wq, Ws, bgu, cnt, off, rows, T, H, E, k, I, h, s));
+  return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+}
+
+static int run_down_mx(const char* fn, const void* h, const void* Wq, const void* Ws, const void* bd,
+                       const int32_t* cnt, const int32_t* off, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                       float* o, int32_t path, hipStream_t s) {
+  path = choose_path(path, T, E, k);
+  if (path == MOE_PATH_GEMV)
+    return hip_status(fn, moe::launch_mxfp4_down(h, Wq, Ws, bd, cnt, off, T, H, E, k, I, o, s));
+  if (path == MOE_PATH_GEMM)
+    return hip_status(fn, moe::launch_gemm_mxfp4_down(h, Wq, Ws, bd, cnt, off, T, H, E, k, I, o, s));
+  return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+}
+
+int moe_forward_mxfp4_ex(const void* x, const void* Wr, const void* br, const void* Wgu_q, const void* Wgu_s,
+                         const void* bgu, const void* Wd_q, const void* Wd_s, const void* bd, int64_t T, int32_t H,
+                         int32_t E, int32_t k, int32_t I, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                         void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
   const char* fn = "moe_forward_mxfp4";
   if (int st = check_dims(fn, T, H, E, k, I)) return st;
   if (int st = check_mx_dims(fn, H, I)) return st;
@@ -367,6 +389,8 @@ int moe_forward_mxfp4(const void* x, const void* Wr, const void* br, const void*
     return fail(MOE_ERR_INVALID_ARG, "%s: topk_ids_out is not 4-byte aligned", fn);
   if (topk_w_out && !aligned(topk_w_out, 4))
     return fail(MOE_ERR_INVALID_ARG, "%s: topk_w_out is not 4-byte aligned", fn);
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
   if (T == 0) return ok();
   const Layout L = layout(T, H, E, k, I);
   if (workspace == nullptr || workspace_bytes < L.total)
@@ -388,16 +412,23 @@ int moe_forward_mxfp4(const void* x, const void* Wr, const void* br, const void*
 
   if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, ids, w, MOE_ROUTE_AUTO, s))) return st;
   if (int st = hip_status(fn, moe::launch_permute(ids, T, E, k, cnt, off, rows, pos, s))) return st;
-  if (int st = hip_status(fn, moe::launch_mxfp4_gate_up(x, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, E, k, I, h, s)))
-    return st;
-  if (int st = hip_status(fn, moe::launch_mxfp4_down(h, Wd_q, Wd_s, bd, cnt, off, T, H, E, k, I, o, s))) return st;
+  if (int st = run_gate_up_mx(fn, x, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, E, k, I, h, path, s)) return st;
+  if (int st = run_down_mx(fn, h, Wd_q, Wd_s, bd, cnt, off, T, H, E, k, I, o, path, s)) return st;
   if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s))) return st;
   return ok();
 }
 
+int moe_forward_mxfp4(const void* x, const void* Wr, const void* br, const void* Wgu_q, const void* Wgu_s,
+                      const void* bgu, const void* Wd_q, const void* Wd_s, const void* bd, int64_t T, int32_t H,
+                      int32_t E, int32_t k, int32_t I, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_forward_mxfp4_ex(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, T, H, E, k, I, y, topk_ids_out,
+                              topk_w_out, workspace, workspace_bytes, MOE_PATH_AUTO, stream);
+}
+
 int moe_gate_up_mxfp4(const void* x, const void* Wgu_q, const void* Wgu_s, const void* bgu, const int32_t* cnt,
                       const int32_t* off, const int32_t* rows, int64_t T, int32_t H, int32_t E, int32_t k,
-                      int32_t I, void* h, void* stream) {
+                      int32_t I, void* h, int32_t path, void* stream) {
   const char* fn = "moe_gate_up_mxfp4";
   if (int st = check_dims(fn, T, H, E, k, I)) return st;
   if (int st = check_mx_dims(fn, H, I)) return st;
@@ -409,16 +440,17 @@ int moe_gate_up_mxfp4(const void* x, const void* Wgu_q, const void* Wgu_s, const
   CHECK_PTR(off, 4);
   CHECK_PTR(rows, 4);
   CHECK_PTR(h, 16);
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
   if (T == 0) return ok();
-  if (int st = hip_status(fn, moe::launch_mxfp4_gate_up(x, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, E, k, I, h,
-                                                        (hipStream_t)stream)))
+  if (int st = run_gate_up_mx(fn, x, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, E, k, I, h, path, (hipStream_t)stream))
     return st;
   return ok();
 }
 
 int moe_down_mxfp4(const void* h, const void* Wd_q, const void* Wd_s, const void* bd, const int32_t* cnt,
                    const int32_t* off, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, float* o,
-                   void* stream) {
+                   int32_t path, void* stream) {
   const char* fn = "moe_down_mxfp4";
   if (int st = check_dims(fn, T, H, E, k, I)) return st;
   if (int st = check_mx_dims(fn, H, I)) return st;
@@ -429,10 +461,10 @@ int moe_down_mxfp4(const void* h, const void* Wd_q, const void* Wd_s, const void
   CHECK_PTR(cnt, 4);
   CHECK_PTR(off, 4);
   CHECK_PTR(o, 16);
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
   if (T == 0) return ok();
-  if (int st = hip_status(fn, moe::launch_mxfp4_down(h, Wd_q, Wd_s, bd, cnt, off, T, H, E, k, I, o,
-                                                     (hipStream_t)stream)))
-    return st;
+  if (int st = run_down_mx(fn, h, Wd_q, Wd_s, bd, cnt, off, T, H, E, k, I, o, path, (hipStream_t)stream)) return st;
   return ok();
 }
 

@@ -50,6 +50,18 @@ def assert_y_close(y: np.ndarray, ref: np.ndarray, what: str = "y", max_rel=Y_MA
     return m
 
 
+def assert_nan_rows(y: np.ndarray, ref: np.ndarray, what: str = "y"):
+    """NaN exactly where the reference has NaN (some rows, all of them
+    present), and the finite rows within the usual bound."""
+    bad_y, bad_ref = np.isnan(y), np.isnan(ref)
+    assert bad_ref.any(), f"{what}: the reference has no NaN"
+    diff = np.argwhere(bad_y != bad_ref)
+    assert diff.size == 0, f"{what}: NaN pattern differs at {diff[:5].tolist()}"
+    rows = ~bad_ref.any(axis=1)
+    assert rows.any(), f"{what}: no finite row left"
+    assert_y_close(y[rows], ref[rows], what)
+
+
 def assert_routing(ids_gpu: np.ndarray, w_gpu: np.ndarray, ids_ref: np.ndarray, w_ref: np.ndarray,
                    logits_ref: np.ndarray | None = None, k: int | None = None):
     bad = np.nonzero((ids_gpu != ids_ref).any(axis=1))[0]

@@ -163,8 +163,12 @@ def test_mxfp4_calls_validate(lib):
         assert b"is NULL" in lib.moe_last_error()
     assert _fwd_mx(lib, ws_bytes=16) == WORKSPACE
     assert _fwd_mx(lib, T=0) == OK
-    assert lib.moe_gate_up_mxfp4(v, v, v, v, v, v, v, 4, 72, 8, 2, 64, v, None) == INVALID
-    assert lib.moe_down_mxfp4(v, v, None, v, v, v, 4, 64, 8, 2, 64, v, None) == INVALID
+    assert lib.moe_gate_up_mxfp4(v, v, v, v, v, v, v, 4, 72, 8, 2, 64, v, 0, None) == INVALID
+    assert lib.moe_down_mxfp4(v, v, None, v, v, v, 4, 64, 8, 2, 64, v, 0, None) == INVALID
+    assert lib.moe_gate_up_mxfp4(v, v, v, v, v, v, v, 4, 64, 8, 2, 64, v, 3, None) == INVALID
+    assert b"unknown path" in lib.moe_last_error()
+    p = [ctypes.c_void_p(FAKE)] * 10
+    assert lib.moe_forward_mxfp4_ex(*p[:9], 8, 64, 8, 2, 64, p[9], None, None, v, 1 << 30, 5, None) == INVALID
     # the quantiser: K % 32 == 0, N % 8 == 0, codes 16-byte aligned
     assert lib.moe_quantize_mxfp4(v, 4, 40, 64, v, v, None) == INVALID and b"K=40" in lib.moe_last_error()
     assert lib.moe_quantize_mxfp4(v, 4, 64, 12, v, v, None) == INVALID and b"N=12" in lib.moe_last_error()

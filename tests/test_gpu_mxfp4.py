@@ -16,7 +16,7 @@ torch = pytest.importorskip("torch")
 
 from moe_layer_route_amd import binding, datagen as d  # noqa: E402
 import oracle.moe_oracle as orc  # noqa: E402
-from checks import assert_routing, assert_y_close, bf16_bits, dev, host_f64  # noqa: E402
+from checks import assert_nan_rows, assert_routing, assert_y_close, bf16_bits, dev, host_f64  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +36,9 @@ def _mx_inputs(cfg, seed=0):
 def _small(T, E, H, I, k, seed=0, router_bias="normal"):
     cfg = d.small_config(T=T, E=E, H=H, I=I, k=k, x_scale=d.scale_for_hidden(H), router_bias=router_bias)
     return cfg, _mx_inputs(cfg, seed)
+
+
+PATHS = ["gemv", "gemm"]
 
 
 def _run(arrays, k, **kw):
@@ -88,19 +91,23 @@ def test_quantize_matches_oracle(E, K, N):
     (200, 16, 256, 160, 4),   # 2I = 320 and H = 256: partial column slices; two 16-row chunks a pass
     (17, 32, 2880, 2880, 4),  # full hidden and intermediate sizes
     (9, 40, 2880, 224, 8),    # k = 8, E not a power of two, empty experts
+    (300, 4, 160, 608, 4),    # 300 rows per expert: three 128-row tiles; K = 160 is 1.25 quads
+    (257, 8, 2880, 2880, 2),  # ragged M tiles at full size
 ])
-def test_forward_sweep(T, E, H, I, k):
+@pytest.mark.parametrize("path", PATHS)
+def test_forward_sweep(T, E, H, I, k, path):
     _need_gpu()
     cfg, arrays = _small(T, E, H, I, k, seed=T + E)
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    y = _run(arrays, k, topk_ids=ids, topk_w=w)
+    y = _run(arrays, k, topk_ids=ids, topk_w=w, path=path)
     ref = orc.moe_forward_mxfp4(*arrays, k=k)
     assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], ref["logits"], k)
     assert_y_close(host_f64(y), ref["y"], f"y T{T} E{E} H{H} I{I} k{k}")
 
 
-def test_stage_intermediates():
+@pytest.mark.parametrize("path", PATHS)
+def test_stage_intermediates(path):
     """gate_up and down alone against the oracle's h and o, matched through pos."""
     _need_gpu()
     T, E, H, I, k = 45, 8, 2880, 2880, 4
@@ -108,8 +115,8 @@ def test_stage_intermediates():
     x, Wr, br, gq, gs, bgu, dq, ds, bd = [dev(a) for a in arrays]
     ids, w = binding.moe_route(x, Wr, br, k)
     cnt, off, rows, pos = binding.moe_permute(ids, E)
-    h = binding.moe_gate_up_mxfp4(x, gq, gs, bgu, cnt, off, rows, k)
-    o = binding.moe_down_mxfp4(h, dq, ds, bd, cnt, off, T, k)
+    h = binding.moe_gate_up_mxfp4(x, gq, gs, bgu, cnt, off, rows, k, path=path)
+    o = binding.moe_down_mxfp4(h, dq, ds, bd, cnt, off, T, k, path=path)
     y = binding.moe_combine(o, pos, w)
     ref = orc.moe_forward_mxfp4(*arrays, k=k, keep=True)
     p = pos.cpu().numpy()
@@ -132,9 +139,31 @@ def test_skipped_experts_are_never_read():
     bad[7][E - 1] = 255
     bad[5][E - 1] = 0x7FC0       # NaN biases
     bad[8][E - 1] = 0x7FC0
-    y0 = bf16_bits(_run(good, k))
-    y1 = bf16_bits(_run(bad, k))
-    assert (y0 == y1).all()
+    for path in PATHS:
+        y0 = bf16_bits(_run(good, k, path=path))
+        y1 = bf16_bits(_run(bad, k, path=path))
+        assert (y0 == y1).all(), path
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_nan_scale_in_live_expert_propagates(path):
+    """A NaN scale (byte 255) in a selected expert's gate_up and down
+    weights, and a NaN up bias in another: exactly the rows of their tokens
+    are NaN."""
+    _need_gpu()
+    T, E, H, I, k = 40, 8, 96, 160, 2
+    cfg, arrays = _small(T, E, H, I, k, seed=6)
+    x, Wr, br, gq, gs, bgu, dq, ds, bd = arrays
+    ids, _, _ = orc.route(x, Wr, br, k)
+    live = np.unique(ids)
+    gs, ds, bgu = gs.copy(), ds.copy(), bgu.copy()
+    gs[live[0], 1, 2] = 255      # block 1 of gate column 2
+    ds[live[1], 2, 5] = 255      # block 2 of output column 5
+    bgu[live[-1], 3] = 0x7FC0    # up of pair 1
+    args = (x, Wr, br, gq, gs, bgu, dq, ds, bd)
+    y = host_f64(_run(args, k, path=path))
+    ref = orc.moe_forward_mxfp4(*args, k=k)["y"]
+    assert_nan_rows(y, ref)
 
 
 def test_bitwise_repeat_and_poisoned_workspace():
@@ -152,10 +181,11 @@ def test_bitwise_repeat_and_poisoned_workspace():
     assert (outs[0] == outs[1]).all() and (outs[1] == outs[2]).all()
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c4"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c4", "c3", "c5"])
 def test_forward_configs(name):
-    """Decode-sized workloads at full size with MXFP4 experts; c4 (128
-    experts) is checked on a sample of tokens."""
+    """Every workload at full size with MXFP4 experts; the oracle checks all
+    tokens at E = 32 decode sizes and a sample of tokens otherwise (the
+    hottest expert's tokens included at the prefill sizes)."""
     _need_gpu()
     cfg = d.CONFIGS[name]
     arrays = _mx_inputs(cfg)
@@ -166,7 +196,12 @@ def test_forward_configs(name):
     torch.cuda.synchronize()
     ids_ref, w_ref, lg = orc.route(arrays[0], arrays[1], arrays[2], k)
     assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, lg, k)
-    tokens = np.arange(cfg.T) if cfg.E <= 32 else np.unique(
-        np.concatenate([np.random.default_rng(0).choice(cfg.T, 12, replace=False), [0, cfg.T - 1]]))
+    if cfg.E <= 32 and cfg.T <= 64:
+        tokens = np.arange(cfg.T)
+    else:
+        load = np.bincount(ids_ref.reshape(-1), minlength=cfg.E)
+        hot = np.nonzero((ids_ref == load.argmax()).any(axis=1))[0][:6]
+        tokens = np.unique(np.concatenate([np.random.default_rng(0).choice(cfg.T, 12, replace=False), hot,
+                                           [0, cfg.T - 1]]))
     ref = orc.moe_forward_mxfp4(*arrays, k=k, tokens=tokens)["y"]
     assert_y_close(host_f64(y)[tokens], ref, f"y {name}")

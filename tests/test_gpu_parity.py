@@ -14,7 +14,7 @@ torch = pytest.importorskip("torch")
 
 from moe_layer_route_amd import binding, datagen as d  # noqa: E402
 import oracle.moe_oracle as orc  # noqa: E402
-from checks import assert_routing, assert_y_close, bf16_bits, dev, host_f64  # noqa: E402
+from checks import assert_nan_rows, assert_routing, assert_y_close, bf16_bits, dev, host_f64  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -307,6 +307,24 @@ def test_skipped_experts_are_never_read():
                 continue
             raise
         assert (y0 == y1).all(), path
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_nan_in_live_expert_propagates(path):
+    """A NaN gate bias in one selected expert and a NaN up bias in another:
+    exactly the rows of their tokens are NaN (the GLU's clamps keep NaN)."""
+    _need_gpu()
+    T, E, H, I, k = 31, 8, 136, 72, 2
+    inp = _small_inputs(T, E, H, I, k, seed=6)
+    ids, _, _ = orc.route(inp.x, inp.Wr, inp.br, k)
+    live = np.unique(ids)
+    bgu = inp.bgu.copy()
+    bgu[live[0], 0] = 0x7FC0     # gate of pair 0
+    bgu[live[-1], 3] = 0x7FC0    # up of pair 1
+    args = (inp.x, inp.Wr, inp.br, inp.Wgu, bgu, inp.Wd, inp.bd)
+    y = host_f64(_forward([dev(a) for a in args], k, path=path))
+    ref = orc.moe_forward(*args, k=k)["y"]
+    assert_nan_rows(y, ref)
 
 
 @pytest.mark.parametrize("path", PATHS)
