@@ -35,8 +35,9 @@ Readings where the pages are silent (each is listed in the design doc):
 * R5  the clamped gate value is used in both factors of gate*sigmoid(1.702*gate);
       up is clamped first, then 1 is added.
 
-The MXFP4 weight format (section 5 of the same page) and its readings M1-M3
-are stated next to its functions below.
+The MXFP4 weight format (section 5 of the same page) and its readings M1-M3,
+and the FP8 W8A8 variant (same section) and its readings F1-F6, are stated
+next to their functions below.
 """
 from __future__ import annotations
 
@@ -279,6 +280,149 @@ def moe_forward_mxfp4(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k: int, toke
         return (mxfp4_dequantize(Wgu_q[e], Wgu_s[e]).T, widen(bgu[e]),
                 mxfp4_dequantize(Wd_q[e], Wd_s[e]).T, widen(bd[e]))
     return _forward(x, Wr, br, weights, Wgu_q.shape[1], Wd_q.shape[1], k, tokens, keep, experts)
+
+
+# --------------------------------------------------------------------------
+# FP8 W8A8 (section 5 of the Phase 19 page: 8-bit weights with one scalar
+# scale per expert, stored transposed [E][N][K]; the scales applied after the
+# product).  Readings (listed in the design doc):
+#   F1  the 8-bit format is OCP FP8 E4M3 (bias 7, no infinities, largest
+#       finite 448, S.1111.111 is NaN); conversion to it rounds to nearest
+#       with ties to the even code and saturates to +-448; NaN becomes 0x7F;
+#   F2  a scale is s = amax / 448, and the codes are E4M3(a * (448 / amax)),
+#       each of the three operations in float32 (the precision the codes are
+#       decided in); amax = 0 gives s = 1 and codes of a * 1;
+#   F3  weights: one scale per expert and matrix (amax over the whole
+#       expert), codes stored K-contiguous [E][N][K];
+#   F4  activations ("A8", not specified further): one dynamic scale per row,
+#       a token's row of x for gate_up and a (token, slot) row of h for down;
+#   F5  h is rounded to bf16 (RNE), the type activations are kept in between
+#       the two products, before it is quantised;
+#   F6  each product is sum(code_a * code_w) * s_a * s_w, i.e. the exact
+#       dequantised operands, and then the bias.
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code: int) -> float:
+    """Value of an OCP E4M3 code: bit 7 sign, bits 6..3 exponent (bias 7),
+    bits 2..0 mantissa; exponent 0 is subnormal (m * 2^-9); 0x7F/0xFF NaN."""
+    sign = -1.0 if code & 0x80 else 1.0
+    ex = (code >> 3) & 15
+    man = code & 7
+    if ex == 15 and man == 7:
+        return float("nan")
+    mag = man * 2.0 ** -9 if ex == 0 else (8 + man) * 2.0 ** (ex - 10)
+    return sign * mag
+
+
+E4M3_VALUES = np.array([e4m3_decode(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """float32 values -> E4M3 codes (uint8): nearest value, ties to the even
+    code, magnitudes from 448 up (and infinities) saturated to 448, NaN 0x7F."""
+    v = np.asarray(v, dtype=np.float32).astype(np.float64)
+    a = np.where(np.isnan(v), 0.0, np.abs(v))
+    # quantum of a's binade: 2^(floor(log2 a) - 3) for normals, 2^-9 below 2^-6
+    _, p = np.frexp(np.where(a > 0, a, 1.0))          # a = m * 2^p, m in [0.5, 1)
+    quantum = np.ldexp(1.0, np.maximum(p - 4, -9))
+    q = np.rint(a / quantum) * quantum                  # exact; rint is half-even
+    q = np.minimum(q, E4M3_MAX)
+    _, pq = np.frexp(np.where(q > 0, q, 1.0))
+    normal = q >= 2.0 ** -6
+    ex = np.where(normal, pq - 1 + 7, 0)
+    man = np.where(normal, q / np.ldexp(1.0, pq - 4) - 8, q / 2.0 ** -9)
+    code = (ex.astype(np.int64) << 3) | man.astype(np.int64)
+    code = code | (np.signbit(v).astype(np.int64) << 7)
+    code = np.where(np.isnan(v), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def fp8_scale(amax):
+    """(s, inv) for float32 maxima: s = amax / 448, inv = 448 / amax, both
+    rounded to float32; amax = 0 gives (1, 1)."""
+    amax = np.asarray(amax, dtype=np.float32)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(E4M3_MAX), amax)
+    s = np.where(zero, np.float32(1), safe / np.float32(E4M3_MAX)).astype(np.float32)
+    inv = np.where(zero, np.float32(1), np.float32(E4M3_MAX) / safe).astype(np.float32)
+    return s, inv
+
+
+def fp8_quantize_rows(a) -> tuple:
+    """float32 [R][K] (bf16 values) -> (codes uint8 [R][K], s float32 [R]):
+    one scale per row (F2, F4)."""
+    a = np.asarray(a, dtype=np.float32)
+    s, inv = fp8_scale(np.abs(a).max(axis=-1))
+    return e4m3_encode(a * inv[..., None]), s
+
+
+def fp8_quantize_weights(W) -> tuple:
+    """bf16 bits [E][K][N] (x.W form) -> (codes uint8 [E][N][K], s float32 [E]):
+    one scale per expert (F2, F3)."""
+    w = widen(W).astype(np.float32)
+    s, inv = fp8_scale(np.abs(w).reshape(w.shape[0], -1).max(axis=-1))
+    codes = e4m3_encode(w * inv[:, None, None])
+    return np.ascontiguousarray(np.swapaxes(codes, 1, 2)), s
+
+
+def fp8_dequantize(codes, s) -> np.ndarray:
+    """codes [..., R, K] with one scale per leading index -> float64."""
+    return E4M3_VALUES[np.asarray(codes, dtype=np.uint8)] * np.asarray(s, np.float64)[..., None, None]
+
+
+def bf16_round(x) -> np.ndarray:
+    """float64 -> the nearest bf16 value (ties to even), as float64: 8
+    significant bits for normals, a quantum of 2^-133 below 2^-126."""
+    x = np.asarray(x, dtype=np.float64)
+    _, p = np.frexp(np.where(x != 0, x, 1.0))
+    quantum = np.ldexp(1.0, np.maximum(p - 8, -133))
+    return np.where(np.isfinite(x), np.rint(x / quantum) * quantum, x)
+
+
+def fp8_down(hb, Wd_q_e, s_d_e, bd_e64):
+    """Down product of one expert on bf16-rounded h rows (F4-F6): returns the
+    row codes, row scales and o = (codes_h . codes_d^T) * s_h * s_d + bd."""
+    hq, sh = fp8_quantize_rows(hb)
+    o = (E4M3_VALUES[hq] @ E4M3_VALUES[Wd_q_e].T) * (sh.astype(np.float64)[:, None] * float(s_d_e)) + bd_e64
+    return hq, sh, o
+
+
+def moe_forward_fp8(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k: int, tokens=None, keep=False,
+                    experts=None):
+    """The forward with FP8 W8A8 experts: gate_up codes [E][2I][H] with scales
+    [E], down codes [E][H][I] with scales [E].  x rows are quantised per token
+    (F4), h rows per (token, slot) after rounding to bf16 (F5).  Returns what
+    moe_forward returns, plus (keep) the h codes and scales per slot."""
+    sel = slice(None) if tokens is None else np.asarray(tokens)
+    ids, w, lg = route(x[sel], Wr, br, k)
+    xq, sx = fp8_quantize_rows(widen(x[sel]))
+    T = xq.shape[0]
+    E, I2, Hout = Wr.shape[0], Wgu_q.shape[1], Wd_q.shape[1]
+    y = np.zeros((T, Hout))
+    if keep:
+        u_all, h_all, o_all = np.zeros((T * k, I2)), np.zeros((T * k, I2 // 2)), np.zeros((T * k, Hout))
+        hq_all, sh_all = np.zeros((T * k, I2 // 2), np.uint8), np.zeros(T * k, np.float32)
+    flat = ids.reshape(-1)
+    e_lo, e_hi = (0, E) if experts is None else experts
+    for e in range(e_lo, e_hi):
+        slots = np.nonzero(flat == e)[0]
+        if slots.size == 0:
+            continue               # skipped, never multiplied by zero
+        toks = slots // k
+        u = (E4M3_VALUES[xq[toks]] @ E4M3_VALUES[Wgu_q[e]].T) * (sx.astype(np.float64)[toks, None]
+                                                                  * float(Wgu_s[e])) + widen(bgu[e])
+        h = clamped_glu(u)
+        hq, sh, o = fp8_down(bf16_round(h), Wd_q[e], Wd_s[e], widen(bd[e]))
+        np.add.at(y, toks, w.reshape(-1)[slots][:, None] * o)
+        if keep:
+            u_all[slots], h_all[slots], o_all[slots] = u, h, o
+            hq_all[slots], sh_all[slots] = hq, sh
+    out = {"y": y, "ids": ids, "w": w, "logits": lg, "sx": sx}
+    if keep:
+        out.update(u=u_all, h=h_all, o=o_all, hq=hq_all, sh=sh_all, xq=xq)
+    return out
 
 
 # --------------------------------------------------------------------------

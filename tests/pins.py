@@ -474,7 +474,199 @@ def pin_mxfp4_forward(orc):
         assert np.abs(got - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max()), n
 
 
+# ---------------------------------------------------------------------------
+# FP8 W8A8 (section 5 of the Phase 19 page: 8-bit weights with one scale per
+# expert; the OCP E4M3 format: sign, 4 exponent bits with bias 7, 3 mantissa
+# bits, no infinities, S.1111.111 NaN, largest finite 1.75 * 2^8 = 448)
+# ---------------------------------------------------------------------------
+E4M3_KNOWN = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0,
+              0x3F: 1.875, 0x40: 2.0, 0x77: 240.0, 0x78: 256.0, 0x7E: 448.0, 0x80: -0.0, 0xB8: -1.0,
+              0xC0: -2.0, 0xFE: -448.0}
+
+
+def pin_e4m3_table(orc):
+    """Values of the OCP E4M3 format: fixed points, the two NaNs, monotone
+    positive codes, negative codes the mirror of the positive ones."""
+    t = orc.E4M3_VALUES
+    for c, v in E4M3_KNOWN.items():
+        assert t[c] == v and math.copysign(1, t[c]) == math.copysign(1, v), (hex(c), t[c], v)
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF]) and np.isnan(t).sum() == 2
+    assert (np.diff(t[:0x7F]) > 0).all()
+    assert (t[0x80:0xFF] == -t[:0x7F]).all()
+
+
+def _e4m3_nearest(v):
+    """Brute force: nearest finite E4M3 value by table search, ties to the
+    even code, saturation above 448, NaN -> 0x7F, the sign of zero kept."""
+    table = [E4M3_KNOWN_VALUE(c) for c in range(256)]
+    out = []
+    for x in np.asarray(v, dtype=np.float32).tolist():
+        if math.isnan(x):
+            out.append(0x7F)
+            continue
+        neg = math.copysign(1, x) < 0
+        a = min(abs(x), 448.0)
+        cands = [c for c in range(0x7F)]
+        dist = [abs(a - table[c]) for c in cands]
+        best = min(dist)
+        tie = [c for c, d in zip(cands, dist) if d == best]
+        pick = [c for c in tie if c % 2 == 0] or tie
+        out.append(pick[0] | (0x80 if neg else 0))
+    return np.array(out, dtype=np.uint8)
+
+
+def E4M3_KNOWN_VALUE(c):
+    """E4M3 value from the format's definition (independent of the oracle)."""
+    sign = -1.0 if c & 0x80 else 1.0
+    e, m = (c >> 3) & 15, c & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    return sign * (m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+
+
+def pin_e4m3_encode(orc):
+    """The encoder equals the table search on values of every magnitude,
+    exact midpoints (ties), values just past them, saturation and specials."""
+    rng = np.random.default_rng(53)
+    v = (rng.normal(0, 1, 600) * np.exp2(rng.integers(-13, 11, 600))).astype(np.float32)
+    fin = np.array([E4M3_KNOWN_VALUE(c) for c in range(0x7E)])
+    mids = ((fin[1:] + fin[:-1]) / 2).astype(np.float32)
+    nudge = np.nextafter(mids, np.float32(np.inf), dtype=np.float32)
+    special = np.array([0.0, -0.0, 448.0, 449.0, 463.9, 464.0, 500.0, 1e30, np.inf, -np.inf, np.nan, -1e-30,
+                        2.0 ** -10, 3 * 2.0 ** -10, -(2.0 ** -10)], dtype=np.float32)
+    allv = np.concatenate([v, mids, -mids, nudge, special])
+    got = orc.e4m3_encode(allv)
+    ref = _e4m3_nearest(allv)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(allv[i]), hex(got[i]), hex(ref[i])) for i in bad[:5]]
+
+
+def pin_fp8_scales(orc):
+    """s = amax / 448 and inv = 448 / amax in float32; amax 0 -> (1, 1);
+    row quantisation: fixed codes, row independence, power-of-two scaling."""
+    s, inv = orc.fp8_scale(np.array([448.0, 896.0, 1.0, 0.0, 3.5], np.float32))
+    assert list(s[[0, 1, 3, 4]]) == [1.0, 2.0, 1.0, 2.0 ** -7] and s[2] == np.float32(1.0) / np.float32(448.0)
+    assert list(inv) == [1.0, 0.5, 448.0, 1.0, 128.0]
+    rows = np.array([[448.0, -224.0, 1.0, 0.0], [3.5, 0.0, -1.75, 2.0 ** -7]], np.float32)
+    codes, sc = orc.fp8_quantize_rows(rows)
+    assert list(codes[0]) == [0x7E, 0xF6, 0x38, 0x00] and sc[0] == 1.0
+    assert list(codes[1]) == [0x7E, 0x00, 0xF6, 0x38] and sc[1] == 2.0 ** -7
+    rng = np.random.default_rng(59)
+    a = (rng.normal(0, 1, (6, 40)) * np.exp2(rng.integers(-8, 8, (6, 1)))).astype(np.float32)
+    c_all, s_all = orc.fp8_quantize_rows(a)
+    for r in range(a.shape[0]):
+        c1, s1 = orc.fp8_quantize_rows(a[r:r + 1])
+        assert (c1[0] == c_all[r]).all() and s1[0] == s_all[r], r
+        c2, s2 = orc.fp8_quantize_rows(a[r:r + 1] * np.float32(16.0))
+        assert (c2[0] == c_all[r]).all() and s2[0] == 16 * s_all[r], r
+    d = orc.E4M3_VALUES[c_all] * s_all[:, None]
+    assert (np.abs(d - a) <= np.abs(a) * 2.0 ** -4 + s_all[:, None] * 2.0 ** -10).all()
+
+
+def pin_fp8_weight_layout(orc):
+    """Codes are K-contiguous [E][N][K] with W[e][k][n] at codes[e][n][k];
+    one scale per expert (a 4x larger expert has the same codes, 4x s)."""
+    E, K, N = 2, 16, 8
+    rng = np.random.default_rng(61)
+    base = rng.choice([E4M3_KNOWN_VALUE(c) for c in range(0x30, 0x7E)], (K, N))
+    base[3, 5] = 448.0
+    w = np.stack([base, 4 * base])
+    codes, s = orc.fp8_quantize_weights(_bf(w))
+    assert codes.shape == (E, N, K) and list(s) == [1.0, 4.0]
+    assert (codes[0] == codes[1]).all()
+    for k, n in [(0, 0), (3, 5), (15, 7), (7, 2)]:
+        assert E4M3_KNOWN_VALUE(int(codes[0, n, k])) == base[k, n], (k, n)
+
+
+def _fp8_exact_inputs(orc, seed, T, E, H, I):
+    """bf16 inputs whose FP8 quantisation is exact: every x row and every
+    expert's weights hold E4M3 values times a power of two, with the row or
+    expert maximum at 448 times that power."""
+    rng = np.random.default_rng(seed)
+    vals = np.array([E4M3_KNOWN_VALUE(c) for c in range(0x28, 0x7E)])
+    def exact(shape, maxpos, p2):
+        a = rng.choice(vals, shape) * rng.choice([-1.0, 1.0], shape)
+        a[maxpos] = 448.0
+        return a * p2
+    x = np.stack([exact((H,), 0, 2.0 ** rng.integers(-9, -6)) for _ in range(T)])
+    Wgu = np.stack([exact((H, 2 * I), (0, 0), 2.0 ** rng.integers(-14, -11)) for _ in range(E)])
+    Wd = np.stack([exact((I, H), (0, 0), 2.0 ** rng.integers(-14, -11)) for _ in range(E)])
+    Wr = _bf(rng.normal(0, 0.3, (E, H)))
+    br = _bf(rng.normal(0, 0.3, E))
+    bgu = _bf(rng.normal(0, 0.5, (E, 2 * I)))
+    bd = _bf(rng.normal(0, 0.5, (E, H)))
+    return _bf(x), Wr, br, _bf(Wgu), bgu, _bf(Wd), bd
+
+
+def pin_fp8_gate_up_exact(orc):
+    """With exactly quantisable x and weights, the FP8 gate_up pre-activations
+    equal the bf16 forward's (pinned to brute force above)."""
+    T, E, H, I, k = 6, 4, 64, 32, 2
+    x, Wr, br, Wgu, bgu, Wd, bd = _fp8_exact_inputs(orc, 67, T, E, H, I)
+    gq, gs = orc.fp8_quantize_weights(Wgu)
+    dq, ds = orc.fp8_quantize_weights(Wd)
+    got = orc.moe_forward_fp8(x, Wr, br, gq, gs, bgu, dq, ds, bd, k=k, keep=True)
+    ref = orc.moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k=k, keep=True)
+    assert "u" in got and "u" in ref, "intermediates missing"
+    assert (got["ids"] == ref["ids"]).all()
+    assert np.abs(got["u"] - ref["u"]).max() <= 1e-12 * np.abs(ref["u"]).max()
+    assert (orc.fp8_dequantize(gq, gs) == np.swapaxes(bf16_bits_to_f32(Wgu), 1, 2)).all()
+
+
+def pin_fp8_down_exact(orc):
+    """The down product on exactly quantisable h rows (the row maximum 448
+    times a power of two) equals the plain float64 product plus bias; bf16
+    rounding is to nearest, ties to even."""
+    rng = np.random.default_rng(71)
+    vals = np.array([E4M3_KNOWN_VALUE(c) for c in range(0x20, 0x7E)])
+    I, H = 32, 24
+    hb = rng.choice(vals, (5, I)) * rng.choice([-1.0, 1.0], (5, I))
+    hb[:, 3] = 448.0
+    hb *= np.exp2(rng.integers(-10, 3, (5, 1)))
+    Wd = rng.choice(vals, (1, I, H)) * 2.0 ** -12
+    Wd[0, 0, 0] = 448.0 * 2.0 ** -12
+    bd = rng.normal(0, 0.5, H)
+    dq, ds = orc.fp8_quantize_weights(_bf(Wd))
+    hq, sh, o = orc.fp8_down(hb, dq[0], ds[0], bd)
+    ref = hb @ Wd[0] + bd
+    assert np.abs(o - ref).max() <= 1e-12 * np.abs(ref).max()
+    r = orc.bf16_round(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -30, -(1 + 2.0 ** -8),
+                                 2.0 ** -130 + 2.0 ** -134, 3.0e38, 0.0]))
+    assert list(r) == [1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -1.0, 2.0 ** -130, float(np.float32(_bf_val(3.0e38))), 0.0]
+
+
+def _bf_val(v):
+    return bf16_bits_to_f32(_bf(np.array([v])))[0]
+
+
+def pin_fp8_forward_structure(orc):
+    """On random inputs: each slot's h codes and scale are that row's own
+    quantisation after bf16 rounding; x scales are per token; a sample of
+    tokens gives the same rows as the whole batch; y stays within FP8
+    quantisation error of the bf16 forward."""
+    T, E, H, I, k = 7, 6, 64, 32, 3
+    x, Wr, br, Wgu, bgu, Wd, bd = _tiny_inputs(73, T, E, H, I, 1.5)
+    gq, gs = orc.fp8_quantize_weights(Wgu)
+    dq, ds = orc.fp8_quantize_weights(Wd)
+    args = (x, Wr, br, gq, gs, bgu, dq, ds, bd)
+    got = orc.moe_forward_fp8(*args, k=k, keep=True)
+    assert all(key in got for key in ("h", "hq", "sh", "sx")), "intermediates missing"
+    for slot in range(T * k):
+        c, sc = orc.fp8_quantize_rows(orc.bf16_round(got["h"][slot:slot + 1]))
+        assert (c[0] == got["hq"][slot]).all() and sc[0] == got["sh"][slot], slot
+    xs = bf16_bits_to_f32(x)
+    for t in range(T):
+        assert got["sx"][t] == np.float32(np.abs(xs[t]).max()) / np.float32(448.0), t
+    sub = [1, 4, 6]
+    part = orc.moe_forward_fp8(*args, k=k, tokens=sub)["y"]
+    assert np.abs(part - got["y"][sub]).max() <= 1e-12 * np.abs(got["y"]).max()
+    ref = orc.moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k=k)["y"]
+    rel = np.abs(got["y"] - ref).sum() / np.abs(ref).sum()
+    assert 1e-4 < rel < 0.15, rel          # E4M3 keeps 3 mantissa bits: a few percent
+
+
 ALL_PINS = [pin_glu, pin_topk, pin_router, pin_permutation, pin_forward_bruteforce,
             pin_identical_experts, pin_structured_experts, pin_skip_semantics, pin_expert_ranges,
             pin_identity_glu_table, pin_e2m1_table, pin_ue8m0, pin_mxfp4_layout, pin_mxfp4_quantize_rne,
-            pin_mxfp4_nearest, pin_mxfp4_forward]
+            pin_mxfp4_nearest, pin_mxfp4_forward, pin_e4m3_table, pin_e4m3_encode, pin_fp8_scales,
+            pin_fp8_weight_layout, pin_fp8_gate_up_exact, pin_fp8_down_exact, pin_fp8_forward_structure]

@@ -10,7 +10,9 @@ import pins
 _real = {n: getattr(orc, n) for n in ("clamped_glu", "router_logits", "select_topk",
                                       "routing_weights", "expert_mlp", "expert_permutation",
                                       "moe_forward", "widen", "mxfp4_quantize", "mxfp4_dequantize",
-                                      "moe_forward_mxfp4", "ue8m0_decode", "e2m1_decode")}
+                                      "moe_forward_mxfp4", "ue8m0_decode", "e2m1_decode", "e4m3_encode",
+                                      "fp8_scale", "fp8_quantize_rows", "fp8_quantize_weights", "bf16_round",
+                                      "moe_forward_fp8", "fp8_down")}
 
 
 def _glu(gate_sel=0, up_sel=1, alpha=1.702, glim=(-np.inf, 7.0), ulim=(-7.0, 7.0), plus=1.0,
@@ -204,7 +206,93 @@ def _forward_mxfp4_untransposed(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k,
     return orc._forward(x, Wr, br, weights, Wgu_q.shape[1], Wd_q.shape[1], k, tokens, keep, experts)
 
 
+def _e4m3_table_bias8():
+    t = np.array(orc.E4M3_VALUES, copy=True)
+    return t / 2.0
+
+
+def _encode_variant(ties="even", saturate=True):
+    def f(v):
+        shape = np.shape(v)
+        v = np.asarray(v, dtype=np.float32).astype(np.float64).reshape(-1)
+        fin = orc.E4M3_VALUES[:0x7F]
+        a = np.where(np.isnan(v), 0.0, np.abs(v))
+        if saturate:
+            a = np.minimum(a, 448.0)
+        d = np.abs(a[:, None] - fin[None, :])
+        best = d.min(axis=1, keepdims=True)
+        cand = d == best
+        if ties == "even":
+            pick = cand & (np.arange(0x7F) % 2 == 0)
+            code = np.where(pick.any(1), pick.argmax(1), cand.argmax(1))
+        else:                                     # ties away from zero
+            code = 0x7E - cand[:, ::-1].argmax(1)
+        code = np.where(a > 464.0, 0x7F, code)    # (no saturation: overflow is NaN)
+        code = code | (np.signbit(v).astype(np.int64) << 7)
+        return np.where(np.isnan(v), 0x7F, code).astype(np.uint8).reshape(shape)
+    return f
+
+
+def _fp8_scale_inverted(amax):
+    s, inv = _real["fp8_scale"](amax)
+    return inv, s
+
+
+def _fp8_rows_per_tensor(a):
+    a = np.asarray(a, dtype=np.float32)
+    s, inv = orc.fp8_scale(np.abs(a).max())
+    return orc.e4m3_encode(a * inv), np.full(a.shape[:-1], s, np.float32)
+
+
+def _fp8_weights_untransposed(W):
+    codes, s = _real["fp8_quantize_weights"](W)
+    return np.ascontiguousarray(np.swapaxes(codes, 1, 2)).reshape(codes.shape), s
+
+
+def _fp8_weights_one_scale(W):
+    w = orc.widen(W).astype(np.float32)
+    s, inv = orc.fp8_scale(np.abs(w).max())
+    codes = orc.e4m3_encode(w * inv)
+    return np.ascontiguousarray(np.swapaxes(codes, 1, 2)), np.full(w.shape[0], s, np.float32)
+
+
+def _bf16_round_truncating(x):
+    x = np.asarray(x, dtype=np.float64)
+    _, p = np.frexp(np.where(x != 0, x, 1.0))
+    q = np.ldexp(1.0, np.maximum(p - 8, -133))
+    return np.trunc(x / q) * q
+
+
+def _forward_fp8_variant(round_h=True, weight_scale=True):
+    def f(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k, tokens=None, keep=False, experts=None):
+        gs = Wgu_s if weight_scale else np.ones_like(Wgu_s)
+        saved = orc.bf16_round
+        if not round_h:
+            orc.bf16_round = lambda v: np.asarray(v, dtype=np.float64)
+        try:
+            return _real["moe_forward_fp8"](x, Wr, br, Wgu_q, gs, bgu, Wd_q, Wd_s, bd, k, tokens, keep, experts)
+        finally:
+            orc.bf16_round = saved
+    return f
+
+
+def _fp8_down_no_weight_scale(hb, Wd_q_e, s_d_e, bd_e64):
+    return _real["fp8_down"](hb, Wd_q_e, np.float32(1.0), bd_e64)
+
+
 MUTANTS = {
+    "e4m3_exponent_bias_8": ("E4M3_VALUES", _e4m3_table_bias8()),
+    "e4m3_encode_ties_away": ("e4m3_encode", _encode_variant(ties="away")),
+    "e4m3_encode_overflow_nan": ("e4m3_encode", _encode_variant(saturate=False)),
+    "fp8_scale_inverted": ("fp8_scale", _fp8_scale_inverted),
+    "fp8_rows_one_scale_per_tensor": ("fp8_quantize_rows", _fp8_rows_per_tensor),
+    "fp8_weights_untransposed": ("fp8_quantize_weights", _fp8_weights_untransposed),
+    "fp8_weights_one_scale_for_all_experts": ("fp8_quantize_weights", _fp8_weights_one_scale),
+    "bf16_round_truncating": ("bf16_round", _bf16_round_truncating),
+    "fp8_forward_h_not_rounded_to_bf16": ("moe_forward_fp8", _forward_fp8_variant(round_h=False)),
+    "fp8_forward_gate_up_scale_dropped": ("moe_forward_fp8", _forward_fp8_variant(weight_scale=False)),
+    "fp8_down_scale_dropped": ("fp8_down", _fp8_down_no_weight_scale),
+
     "e2m1_table_typo": ("E2M1_VALUES", _e2m1_table_typo()),
     "e2m1_exponent_bias_0": ("e2m1_decode", _e2m1_decode_bias0),
     "ue8m0_bias_128": ("ue8m0_decode", _ue8m0_bias128),
