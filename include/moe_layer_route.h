@@ -320,6 +320,89 @@ MOE_API int moe_down_mxfp4(const void* h, const void* Wd_q, const void* Wd_s, co
                            int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, float* o,
                            int32_t path, void* stream);
 
+/*
+ * FP8 W8A8 experts -- xserv "Phase 19: gpt-oss-20b MoE support", section 5:
+ * 8-bit weights with one scalar scale per expert, stored transposed
+ * ([E][N][K], the contraction dimension contiguous), and 8-bit activations;
+ * the scales are applied after the product.  Router, biases and outputs stay
+ * as in moe_forward.
+ *
+ * Format: OCP FP8 E4M3 -- bit 7 sign, bits 6-3 exponent (bias 7), bits 2-0
+ * mantissa; exponent 0 is subnormal (m * 2^-9); largest finite 448; 0x7F and
+ * 0xFF are NaN; no infinities.  A tensor slice with maximum |a| = amax has
+ * the float32 scale s = amax / 448 and the codes E4M3(a * (448 / amax)),
+ * each operation rounded in float32, E4M3 rounding to nearest with ties to
+ * the even code and saturating at 448 (NaN -> 0x7F); amax = 0 gives s = 1.
+ * The value of a code is E4M3(code) * s.
+ *   Weights:     one scale per expert and matrix.
+ *   Activations: one scale per row: a token's row of x for gate_up, a (token,
+ *                slot) row of h for down, where h is first rounded to bf16.
+ * gate_up = (codes_x . codes_W) * s_x[t] * s_W[e] + bias (the float32 sum of
+ * exact code products), then the clamped GLU as in moe_forward; down likewise
+ * with the h codes.  Requires H % 16 == 0 and I % 16 == 0; code arrays
+ * 16-byte aligned, scale arrays 4-byte aligned.
+ */
+
+/*
+ * moe_quantize_fp8 -- bf16 weights W [E][K][N] (x.W form, as in moe_forward)
+ * to codes [E][N][K] and one scale per expert.  K % 16 == 0, N % 8 == 0.
+ *   W       bf16 [E][K][N]     in
+ *   codes   uint8 [E][N][K]    out
+ *   scales  float32 [E]        out (also used as scratch during the call)
+ */
+MOE_API int moe_quantize_fp8(const void* W, int32_t E, int32_t K, int32_t N, void* codes, float* scales,
+                             void* stream);
+
+/*
+ * moe_quantize_rows_fp8 -- bf16 rows a [R][K] to codes [R][K] and one scale
+ * per row (the activation quantisation moe_forward_fp8 applies to x and h).
+ * K % 16 == 0; R = 0 is a no-op.
+ */
+MOE_API int moe_quantize_rows_fp8(const void* a, int64_t R, int32_t K, void* codes, float* scales, void* stream);
+
+/* Bytes of workspace moe_forward_fp8 needs: moe_workspace_bytes plus the x
+ * and h codes and their row scales (T*H + T*k*I bytes and 4*(T + T*k)). */
+MOE_API size_t moe_workspace_bytes_fp8(int64_t T, int32_t H, int32_t E, int32_t k, int32_t I);
+
+/*
+ * moe_forward_fp8 -- moe_forward with FP8 W8A8 experts:
+ *   Wgu_q uint8 [E][2I][H], Wgu_s float32 [E]   gate_up (columns interleaved
+ *                          gate0, up0, gate1, ... as in moe_forward)
+ *   Wd_q  uint8 [E][H][I],  Wd_s  float32 [E]   down
+ * x is quantised per token and h per (token, slot) row on the device, inside
+ * the call.  Every other argument and output is as in moe_forward; the
+ * workspace must hold moe_workspace_bytes_fp8(...) bytes.  Expert paths:
+ * MOE_PATH_GEMM is the LDS-tiled grouped GEMM on the FP8 matrix cores;
+ * MOE_PATH_GEMV returns MOE_ERR_UNSUPPORTED; AUTO takes MOE_PATH_GEMM.
+ */
+MOE_API int moe_forward_fp8(const void* x, const void* Wr, const void* br,
+                            const void* Wgu_q, const float* Wgu_s, const void* bgu,
+                            const void* Wd_q, const float* Wd_s, const void* bd,
+                            int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                            void* y, int32_t* topk_ids_out, float* topk_w_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_forward_fp8 with the expert path forced (MOE_PATH_*). */
+MOE_API int moe_forward_fp8_ex(const void* x, const void* Wr, const void* br,
+                               const void* Wgu_q, const float* Wgu_s, const void* bgu,
+                               const void* Wd_q, const float* Wd_s, const void* bd,
+                               int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                               void* y, int32_t* topk_ids_out, float* topk_w_out,
+                               void* workspace, size_t workspace_bytes, int32_t path, void* stream);
+
+/* Stage calls of moe_forward_fp8.  gate_up takes the x codes and row scales
+ * (moe_quantize_rows_fp8 of x: xq [T][H], sx [T]) and writes bf16 h as
+ * moe_gate_up does; down takes the h codes and row scales (hq [T*k][I], sh
+ * [T*k], in the permuted row order of h) and writes o as moe_down does. */
+MOE_API int moe_gate_up_fp8(const void* xq, const float* sx, const void* Wgu_q, const float* Wgu_s,
+                            const void* bgu, const int32_t* cnt, const int32_t* off, const int32_t* rows,
+                            int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, void* h,
+                            int32_t path, void* stream);
+MOE_API int moe_down_fp8(const void* hq, const float* sh, const void* Wd_q, const float* Wd_s,
+                         const void* bd, const int32_t* cnt, const int32_t* off,
+                         int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, float* o,
+                         int32_t path, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

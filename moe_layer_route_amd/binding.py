@@ -26,7 +26,8 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace
            "moe_route", "moe_route_ex",
            "moe_forward", "moe_forward_ex", "moe_forward_ep", "moe_permute", "moe_gate_up", "moe_down",
            "moe_combine", "moe_quantize_mxfp4", "moe_forward_mxfp4", "moe_forward_mxfp4_ex", "moe_gate_up_mxfp4",
-           "moe_down_mxfp4")
+           "moe_down_mxfp4", "moe_quantize_fp8", "moe_quantize_rows_fp8", "moe_workspace_bytes_fp8",
+           "moe_forward_fp8", "moe_forward_fp8_ex", "moe_gate_up_fp8", "moe_down_fp8")
 
 
 class MoEError(RuntimeError):
@@ -57,6 +58,13 @@ _SIGS = {
     "moe_forward_mxfp4_ex": (ctypes.c_int, [_vp] * 9 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _i32, _vp]),
     "moe_gate_up_mxfp4": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
     "moe_down_mxfp4": (ctypes.c_int, [_vp] * 6 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
+    "moe_quantize_fp8": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "moe_quantize_rows_fp8": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp]),
+    "moe_workspace_bytes_fp8": (_sz, [_i64, _i32, _i32, _i32, _i32]),
+    "moe_forward_fp8": (ctypes.c_int, [_vp] * 9 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _vp]),
+    "moe_forward_fp8_ex": (ctypes.c_int, [_vp] * 9 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _i32, _vp]),
+    "moe_gate_up_fp8": (ctypes.c_int, [_vp] * 8 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
+    "moe_down_fp8": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
 }
 
 
@@ -324,3 +332,109 @@ def moe_down_mxfp4(h, Wd_q, Wd_s, bd, cnt, off, T: int, k: int, o=None, path="au
     _check(library().moe_down_mxfp4(_ptr(h), _ptr(Wd_q), _ptr(Wd_s), _ptr(bd), _ptr(cnt), _ptr(off), T, H, E,
                                     k, I, _ptr(o), path_code(path), _stream(stream)), "moe_down_mxfp4")
     return o[:T * k]
+
+
+# ---------------------------------------------------------------------------
+# FP8 W8A8
+# ---------------------------------------------------------------------------
+def _f32(*ts):
+    for t in ts:
+        if t.dtype != torch.float32:
+            raise MoEError(f"expected a float32 tensor, got {t.dtype}")
+
+
+def workspace_bytes_fp8(T: int, H: int, E: int, k: int, I: int) -> int:
+    return int(library().moe_workspace_bytes_fp8(T, H, E, k, I))
+
+
+def alloc_workspace_fp8(T: int, H: int, E: int, k: int, I: int, device=None) -> torch.Tensor:
+    n = workspace_bytes_fp8(T, H, E, k, I)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def moe_quantize_fp8(W, codes=None, scales=None, stream=None):
+    """bf16 weights [E][K][N] (x.W form) -> (codes uint8 [E][N][K], scales float32 [E])."""
+    _dev(W)
+    _b16(W)
+    E, K, N = W.shape
+    if codes is None:
+        codes = torch.empty((E, N, K), dtype=torch.uint8, device=W.device)
+    if scales is None:
+        scales = torch.empty((E,), dtype=torch.float32, device=W.device)
+    _dev(codes, scales)
+    _u8(codes)
+    _f32(scales)
+    _check(library().moe_quantize_fp8(_ptr(W), E, K, N, _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_quantize_fp8")
+    return codes, scales
+
+
+def moe_quantize_rows_fp8(a, codes=None, scales=None, stream=None):
+    """bf16 rows [R][K] -> (codes uint8 [R][K], scales float32 [R])."""
+    _dev(a)
+    _b16(a)
+    R, K = a.shape
+    if codes is None:
+        codes = torch.empty((R, K), dtype=torch.uint8, device=a.device)
+    if scales is None:
+        scales = torch.empty((R,), dtype=torch.float32, device=a.device)
+    _dev(codes, scales)
+    _u8(codes)
+    _f32(scales)
+    _check(library().moe_quantize_rows_fp8(_ptr(a), R, K, _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_quantize_rows_fp8")
+    return codes, scales
+
+
+def moe_forward_fp8(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k: int = 4, y=None, workspace=None,
+                    topk_ids=None, topk_w=None, path="auto", stream=None):
+    """moe_forward with FP8 W8A8 experts; returns y (bf16 [T,H])."""
+    _dev(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd)
+    _b16(x, Wr, br, bgu, bd)
+    _u8(Wgu_q, Wd_q)
+    _f32(Wgu_s, Wd_s)
+    T, H = x.shape
+    E = Wr.shape[0]
+    I = Wd_q.shape[2]
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace_fp8(T, H, E, k, I, x.device)
+    _dev(y, workspace, topk_ids, topk_w)
+    st = library().moe_forward_fp8_ex(_ptr(x), _ptr(Wr), _ptr(br), _ptr(Wgu_q), _ptr(Wgu_s), _ptr(bgu),
+                                      _ptr(Wd_q), _ptr(Wd_s), _ptr(bd), T, H, E, k, I, _ptr(y), _ptr(topk_ids),
+                                      _ptr(topk_w), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      path_code(path), _stream(stream))
+    _check(st, "moe_forward_fp8")
+    return y
+
+
+def moe_gate_up_fp8(xq, sx, Wgu_q, Wgu_s, bgu, cnt, off, rows, k: int, h=None, path="auto", stream=None):
+    """FP8 gate_up + bias + GLU from x codes and row scales; returns h (bf16 [T*k, I], permuted order)."""
+    _dev(xq, sx, Wgu_q, Wgu_s, bgu, cnt, off, rows)
+    _u8(xq, Wgu_q)
+    _f32(sx, Wgu_s)
+    T, H = xq.shape
+    E = Wgu_q.shape[0]
+    I = Wgu_q.shape[1] // 2
+    if h is None:
+        h = torch.empty((T * k, I), dtype=torch.bfloat16, device=xq.device)
+    _dev(h)
+    _check(library().moe_gate_up_fp8(_ptr(xq), _ptr(sx), _ptr(Wgu_q), _ptr(Wgu_s), _ptr(bgu), _ptr(cnt), _ptr(off),
+                                     _ptr(rows), T, H, E, k, I, _ptr(h), path_code(path), _stream(stream)),
+           "moe_gate_up_fp8")
+    return h
+
+
+def moe_down_fp8(hq, sh, Wd_q, Wd_s, bd, cnt, off, T: int, k: int, o=None, path="auto", stream=None):
+    """FP8 down + bias from h codes and row scales; returns o (float32 [T*k, H], permuted order)."""
+    _dev(hq, sh, Wd_q, Wd_s, bd, cnt, off)
+    _u8(hq, Wd_q)
+    _f32(sh, Wd_s)
+    E, H, I = Wd_q.shape
+    if o is None:
+        o = torch.empty((T * k, H), dtype=torch.float32, device=hq.device)
+    _dev(o)
+    _check(library().moe_down_fp8(_ptr(hq), _ptr(sh), _ptr(Wd_q), _ptr(Wd_s), _ptr(bd), _ptr(cnt), _ptr(off), T, H,
+                                  E, k, I, _ptr(o), path_code(path), _stream(stream)), "moe_down_fp8")
+    return o

@@ -1,0 +1,525 @@
+// FP8 W8A8 experts: the quantisers and the LDS-tiled MFMA grouped GEMMs.
+//
+// xserv "Phase 19: gpt-oss-20b MoE support", section 5 (FP8 W8A8: 8-bit
+// weights with one scalar scale per expert, stored transposed [E][N][K]; one
+// batched launch for all experts with the scales applied after the product),
+// section 2 (gate_up GEMM -> bias -> clamped GLU, down GEMM -> bias) and
+// section 4 (block-uniform early exits, masked tails).
+//
+// Format: OCP FP8 E4M3 (bias 7, largest finite 448, S.1111.111 NaN), the
+// format the gfx950 f8f6f4 MFMAs read with format code 0.  A scale is
+// s = amax / 448 and a code is E4M3(a * (448 / amax)), each in float32, with
+// round-to-nearest-even and saturation at 448; amax = 0 takes s = 1.
+// Weights have one scale per expert; activations one scale per row (a
+// token's x row for gate_up, a (token, slot) row of h for down).  h is
+// rounded to bf16 by the gate_up epilogue and quantised by the row kernel.
+//
+// Tiled GEMM: the bf16 kernel's 128 x 512 tiles, (expert, m-tile) lookup,
+// XCD-aware order, three-buffer token LDS ring and barrier placement, with
+// v_mfma_f32_32x32x64_f8f6f4 (full rate at one wave per SIMD) on K steps of
+// 64 codes.  Each wave owns 128 x 128 = 4 x 4 blocks of 32 x 32.
+//   K slots: operand byte q of lane group g (g = lane/32) is K = 32*(q/16) +
+//   16g + q%16 of the step, for both operands, so every 16-byte load of
+//   either operand is contiguous in memory.
+//   B (codes [E][N][K], K contiguous): lane (c = lane%32, g) of wave w loads,
+//   for block j = 0..3, column n0 + 128w + 4c + j: two 16-byte loads, two
+//   steps ahead in a ring of two register sets, copied out at the step start
+//   so the set can be reloaded at once.
+//   A (codes of token rows): gathered through rows[] (gate_up) or contiguous
+//   (down), two 16-byte pieces per thread three steps ahead, stored into the
+//   fragment-major LDS ring two steps ahead: fragment mi (rows 32mi..32mi+31)
+//   holds, in lane order, the 32 bytes lane l of the MFMA needs.
+// Epilogue: in the 32 x 32 accumulator layout lane l, element v holds row
+// 8*(v/4) + 4*(l/32) + v%4 of MFMA column l%32, i.e. weight column
+// n0 + 128w + 4c + j of block j: a lane holds two whole (gate, up) pairs.
+// Product * s_row * s_expert + bias, then GLU and one 4-byte bf16 h store
+// (gate_up) or one 16-byte float32 store (down).
+#include "device_common.h"
+#include "launch.h"
+
+#include <algorithm>
+#include <type_traits>
+
+namespace moe {
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr float kE4m3Max = 448.0f;
+
+// float -> E4M3 code, nearest with ties to the even code, |v| >= 448 (and
+// infinities) saturated to 448, NaN -> 0x7F.  With e = max(exponent, -6) the
+// quantum of |v|'s binade is 2^(e-3), so q = rint(|v| * 2^(3-e)) (exact
+// scaling, then round-half-even) is the value in quanta, and the code is
+// (e + 6) * 8 + q: for normals that is ((e + 7) << 3) | (q - 8), below 2^-6 it
+// is the subnormal code q, and q = 16 carries into the next binade's m = 0.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), kE4m3Max);
+  const int e = max((int)(__float_as_uint(a) >> 23) - 127, -6);
+  const uint32_t q = (uint32_t)__builtin_rintf(__builtin_amdgcn_ldexpf(a, 3 - e));
+  const uint32_t code = sign | (uint32_t)((e + 6) * 8 + (int)q);
+  return v != v ? 0x7Fu : code;
+}
+
+// (s, inv) of a float32 maximum: s = amax / 448, inv = 448 / amax, each
+// rounded once; amax = 0 gives (1, 1).
+__device__ __forceinline__ void fp8_scale(float amax, float& s, float& inv) {
+  s = amax == 0.0f ? 1.0f : __fdiv_rn(amax, kE4m3Max);
+  inv = amax == 0.0f ? 1.0f : __fdiv_rn(kE4m3Max, amax);
+}
+
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return a | (b << 8) | (c << 16) | (d << 24);
+}
+
+// eight bf16 (one 16-byte piece) * inv -> eight codes (8 bytes)
+__device__ __forceinline__ u32x2_t encode8(u32x4_t v, float inv) {
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[2 * i] = e4m3_encode(bf16lo(v[i]) * inv);
+    c[2 * i + 1] = e4m3_encode(bf16hi(v[i]) * inv);
+  }
+  return u32x2_t{pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])};
+}
+
+// |bf16| maximum of a 16-byte piece, on the bit patterns (a NaN compares
+// above every number, as in a NaN-propagating maximum)
+__device__ __forceinline__ uint32_t absmax8(u32x4_t v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
+  return m;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d, kWave));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Row quantiser: one wave per row of K bf16 (K % 8 == 0): the row maximum,
+// then the codes (the second pass re-reads the row from the cache).
+// ---------------------------------------------------------------------------
+constexpr int kRowWaves = 4;
+
+__global__ __launch_bounds__(kRowWaves * kWave) void fp8_rows_kernel(const bf16_t* __restrict__ a, int64_t R, int K,
+                                                                    uint8_t* __restrict__ codes,
+                                                                    float* __restrict__ scales) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t r = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+  if (r >= R) return;                                    // wave-uniform, no barrier in this kernel
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a + r * K);
+  const int nch = K / 8;
+  uint32_t m = 0;
+  for (int c = lane; c < nch; c += kWave) m = max(m, absmax8(src[c]));
+  m = wave_max(m);
+  float s, inv;
+  fp8_scale(__uint_as_float(m << 16), s, inv);
+  u32x2_t* dst = reinterpret_cast<u32x2_t*>(codes + r * K);
+  for (int c = lane; c < nch; c += kWave) dst[c] = encode8(src[c], inv);
+  if (lane == 0) scales[r] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Weight quantiser, W [E][K][N] bf16 -> codes [E][N][K], one scale per expert.
+// 1. amax[e] = 0 (as bits); 2. atomic maximum of |bits| per expert (order
+// free, so deterministic); 3. quantise and transpose 64 x 64 tiles through
+// LDS; 4. amax -> scale in place.
+// ---------------------------------------------------------------------------
+__global__ void fp8_zero_kernel(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16_t* __restrict__ W, int64_t per_expert,
+                                                      uint32_t* __restrict__ amax) {
+  const int e = blockIdx.y;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(W + (size_t)e * per_expert);
+  const int64_t nch = per_expert / 8;
+  uint32_t m = 0;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nch; c += (int64_t)gridDim.x * blockDim.x)
+    m = max(m, absmax8(src[c]));
+  m = wave_max(m);
+  if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(&amax[e], m << 16);
+}
+
+constexpr int kQt = 64;   // tile: 64 K x 64 N
+
+__global__ __launch_bounds__(256) void fp8_weight_quant_kernel(const bf16_t* __restrict__ W, int K, int N,
+                                                              const uint32_t* __restrict__ amax,
+                                                              uint8_t* __restrict__ codes) {
+  __shared__ float tile[kQt][kQt + 1];
+  const int e = blockIdx.z;
+  const int k0 = blockIdx.y * kQt, n0 = blockIdx.x * kQt;
+  const int t = threadIdx.x;
+  float s, inv;
+  fp8_scale(__uint_as_float(amax[e]), s, inv);
+  const bf16_t* We = W + (size_t)e * K * N;
+  // load: thread t covers row k0 + t/8 (+32) and columns n0 + 8(t%8) .. +7
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kr = t / 8 + 32 * h, nc = 8 * (t % 8);
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    if (k0 + kr < K && n0 + nc < N) v = *reinterpret_cast<const u32x4_t*>(We + (size_t)(k0 + kr) * N + n0 + nc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile[kr][nc + 2 * i] = bf16lo(v[i]);
+      tile[kr][nc + 2 * i + 1] = bf16hi(v[i]);
+    }
+  }
+  __syncthreads();
+  // store: thread t writes column n0 + t/4, K codes k0 + 16(t%4) .. +15
+  const int nc = t / 4, kc = 16 * (t % 4);
+  if (n0 + nc < N && k0 + kc < K) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = pack4(e4m3_encode(tile[kc + 4 * q][nc] * inv), e4m3_encode(tile[kc + 4 * q + 1][nc] * inv),
+                   e4m3_encode(tile[kc + 4 * q + 2][nc] * inv), e4m3_encode(tile[kc + 4 * q + 3][nc] * inv));
+    *reinterpret_cast<u32x4_t*>(codes + ((size_t)e * N + n0 + nc) * K + k0 + kc) = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+}
+
+__global__ void fp8_scale_finalize_kernel(uint32_t* __restrict__ amax_to_scale, int E) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  float s, inv;
+  fp8_scale(__uint_as_float(amax_to_scale[e]), s, inv);
+  amax_to_scale[e] = __float_as_uint(s);
+}
+
+// ---------------------------------------------------------------------------
+// Tiled grouped GEMM
+// ---------------------------------------------------------------------------
+constexpr int kFgThreads = 256;
+constexpr int kFgWaves = kFgThreads / kWave;
+constexpr int kFgBM = 128;
+constexpr int kFgWN = 128;
+constexpr int kFgBN = kFgWaves * kFgWN;   // 512
+constexpr int kFgBK = 64;                 // codes per K step
+constexpr int kFgLdsBufs = 3;
+constexpr int kXcds = 8;
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
+struct FgSmem {
+  u32x4_t a[kFgLdsBufs][kFgBM / 32][kWave][2];   // 3 x 4 fragments x 2 KB
+  float srow[kFgBM];
+};
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_ld16(rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+__device__ __forceinline__ f32x16_t mfma_fp8(const u32x4_t (&a)[2], const u32x4_t (&b)[2], f32x16_t c) {
+  const i32x8_t av = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
+                      (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+  const i32x8_t bv = {(int)b[0].x, (int)b[0].y, (int)b[0].z, (int)b[0].w,
+                      (int)b[1].x, (int)b[1].y, (int)b[1].z, (int)b[1].w};
+  // format 0 (E4M3) for both operands, no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(kFgThreads, 1) void gemm_fp8_kernel(
+    const uint8_t* __restrict__ A,        // gate_up: x codes [T][K]; down: h codes [S][K] (permuted order)
+    const float* __restrict__ a_scale,    // gate_up: [T]; down: [S]
+    const uint8_t* __restrict__ Wq,       // [E][N][K]
+    const float* __restrict__ w_scale,    // [E]
+    const bf16_t* __restrict__ bias,      // [E][N]
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ rows,     // gate_up: permuted slot ids
+    int K, int N, int E, int kslots, int a_rows, int n_tiles, int m_slots, void* __restrict__ out) {
+  __shared__ __align__(16) FgSmem sm;
+  __shared__ int s_tile[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+
+  // ---- block -> (N tile, M-tile slot), consecutive slots on one XCD ----
+  const int per_xcd = gridDim.x / kXcds;
+  const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (L >= n_tiles * m_slots) return;                       // block-uniform
+  const int nt = L / m_slots;
+  const int ms = L - nt * m_slots;
+
+  // ---- M-tile slot -> (expert, first row) ----
+  if (wave == 0) {
+    if (lane == 0) s_tile[0] = -1;
+    int tc[4];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane * 4 + i;
+      tc[i] = e < E ? (cnt[e] + kFgBM - 1) / kFgBM : 0;
+      sum += tc[i];
+    }
+    int start = wave_incl_scan(sum, lane) - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (ms >= start && ms < start + tc[i]) {
+        s_tile[0] = lane * 4 + i;
+        s_tile[1] = (ms - start) * kFgBM;
+      }
+      start += tc[i];
+    }
+  }
+  __syncthreads();
+  const int e = s_tile[0];
+  if (e < 0) return;                                         // block-uniform
+  const int m0 = s_tile[1];
+  const int M = cnt[e];
+  const int row0 = off[e];
+  const int n0 = nt * kFgBN;
+
+  // ---- A: thread t copies pieces p = t and t + 256 of the step: row p/4
+  // (rows past M read row M-1), 16 codes at K offset 16 (p%4); piece c4
+  // belongs to lane group c4%2, operand half c4/2 of fragment row/32 ----
+  const rsrc_t a_rs = make_rsrc(A, (uint32_t)((size_t)a_rows * K));
+  const int a_c4 = tid & 3;
+  uint32_t a_off[2];
+  int a_frag[2], a_lane[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int row = (tid >> 2) + 64 * s;
+    const int m = min(m0 + row, M - 1);
+    const uint32_t r = GATE_UP ? (uint32_t)(rows[row0 + m] / kslots) : (uint32_t)(row0 + m);
+    a_off[s] = r * (uint32_t)K + 16u * a_c4;
+    a_frag[s] = row >> 5;
+    a_lane[s] = (row & 31) + 32 * (a_c4 & 1);
+  }
+  if (tid < kFgBM) {
+    const int m = min(m0 + tid, M - 1);
+    sm.srow[tid] = GATE_UP ? a_scale[rows[row0 + m] / kslots] : a_scale[row0 + m];
+  }
+  // ---- B: lane (c, g) of wave w, block j: column n0 + 128w + 4c + j ----
+  const int g = lane >> 5;
+  const int c = lane & 31;
+  const int cw = n0 + wave * kFgWN + 4 * c;
+  const rsrc_t w_rs = make_rsrc(Wq + (size_t)e * N * K, (uint32_t)N * (uint32_t)K);
+  uint32_t b_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b_off[j] = (uint32_t)min(cw + j, N - 1) * (uint32_t)K + 16u * g;
+
+  auto gload_a = [&](int kt, u32x4_t (&ra)[2]) {
+    const uint32_t kb = (uint32_t)kt * kFgBK;
+    const bool ok = (int)kb + 16 * a_c4 < K;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) ra[s] = buf_ld16(a_rs, ok ? a_off[s] + kb : kOutOfRange);
+  };
+  auto gload_b = [&](int kt, u32x4_t (&rb)[4][2]) {
+    const uint32_t kb = (uint32_t)kt * kFgBK;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bool ok = (int)kb + 32 * h + 16 * g < K;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rb[j][h] = buf_ld16(w_rs, ok ? b_off[j] + kb + 32u * h : kOutOfRange);
+    }
+  };
+  auto lstore = [&](int kt, const u32x4_t (&ra)[2]) {
+    const int buf = kt % kFgLdsBufs;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) sm.a[buf][a_frag[s]][a_lane[s]][a_c4 >> 1] = ra[s];
+  };
+  auto lread = [&](int buf, int mi, u32x4_t (&f)[2]) {
+    f[0] = sm.a[buf][mi][lane][0];
+    f[1] = sm.a[buf][mi][lane][1];
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][j][v] = 0.0f;
+
+  // Registers (the loop is unrolled three times and no ring needs a register
+  // copy): B of steps kt, kt+1, kt+2 (Rb[kt%3] is used by step kt and then
+  // reloaded, at step kt+1, with step kt+3), A of steps kt+2 and kt+3 (Ra,
+  // same ring), the A fragments F of step kt (each reloaded with step kt+1
+  // after its last MFMA).
+  u32x4_t Rb[3][4][2];
+  u32x4_t Ra[3][2];
+  u32x4_t F[4][2];
+
+  // One K step kt (r = kt % 3): issue the loads of A(kt+3), then B(kt+2)
+  // (loads retire in order: the next step's store of A waits for A alone);
+  // multiply B(kt) with F, reading the fragments of kt+1 as those of kt
+  // retire; store A(kt+2); one barrier after the third of the four MFMA
+  // groups.  The LDS ring: buffer (kt+1)%3 is read during step kt, buffer
+  // (kt+2)%3 written before its barrier (its previous reads, of step kt-2,
+  // all precede the barrier of step kt-1).
+  auto step = [&](int kt, auto rc) {
+    constexpr int r = decltype(rc)::value;
+    const u32x4_t (&bt)[4][2] = Rb[r];
+    __builtin_amdgcn_sched_barrier(0);
+    gload_a(kt + 3, Ra[r]);
+    gload_b(kt + 2, Rb[(r + 2) % 3]);
+    const int nbuf = (kt + 1) % kFgLdsBufs;
+    auto group = [&](int mi) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[mi][j] = mfma_fp8(F[mi], bt[j], acc[mi][j]);
+    };
+    group(0);
+    lread(nbuf, 0, F[0]);
+    group(1);
+    lread(nbuf, 1, F[1]);
+    lstore(kt + 2, Ra[(r + 2) % 3]);
+    group(2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 global load
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // 2 LDS reads
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);     // 2 LDS writes
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __syncthreads();
+    lread(nbuf, 2, F[2]);
+    group(3);
+    lread(nbuf, 3, F[3]);
+  };
+
+  // Prologue: the loads in the order the steps issue them (A(j+1), then
+  // B(j)), so the wait counts of the first steps match the later ones.
+  const int nk = (K + kFgBK - 1) / kFgBK;
+  gload_a(0, Ra[0]);
+  gload_a(1, Ra[1]);
+  gload_b(0, Rb[0]);
+  lstore(0, Ra[0]);
+  gload_a(2, Ra[2]);
+  gload_b(1, Rb[1]);
+  lstore(1, Ra[1]);
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) lread(0, mi, F[mi]);
+
+  // The step count is rounded up to the unroll period: an extra step reads
+  // only zeros (K past the end on both operands) and adds exactly 0.
+  const int nk3 = (nk + 2) / 3 * 3;
+  for (int kt = 0; kt < nk3; kt += 3) {
+    step(kt + 0, std::integral_constant<int, 0>{});
+    step(kt + 1, std::integral_constant<int, 1>{});
+    step(kt + 2, std::integral_constant<int, 2>{});
+  }
+
+  // ---- epilogue.  N % 4 == 0 and cw % 4 == 0: a lane's four columns are all
+  // in range or all out of it. ----
+  if (cw >= N) return;                                       // no barrier follows
+  const float ws = w_scale[e];
+  float bb[4];
+  {
+    const uint32_t* bp = reinterpret_cast<const uint32_t*>(bias + (size_t)e * N + cw);
+    const uint32_t b0 = bp[0], b1 = bp[1];
+    bb[0] = bf16lo(b0);
+    bb[1] = bf16hi(b0);
+    bb[2] = bf16lo(b1);
+    bb[3] = bf16hi(b1);
+  }
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rt = 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);   // row within the tile
+      const int m = m0 + rt;
+      if (m < M) {
+        const float sc = sm.srow[rt] * ws;
+        const size_t orow = (size_t)(row0 + m);
+        if (GATE_UP) {
+          const float h0 = clamped_glu(acc[mi][0][v] * sc + bb[0], acc[mi][1][v] * sc + bb[1]);
+          const float h1 = clamped_glu(acc[mi][2][v] * sc + bb[2], acc[mi][3][v] * sc + bb[3]);
+          *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + orow * (N / 2) + cw / 2) =
+              pack_bf16x2(h0, h1);
+        } else {
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + orow * N + cw) =
+              f32x4_t{acc[mi][0][v] * sc + bb[0], acc[mi][1][v] * sc + bb[1], acc[mi][2][v] * sc + bb[2],
+                      acc[mi][3][v] * sc + bb[3]};
+        }
+      }
+    }
+}
+
+template <bool GATE_UP>
+hipError_t launch_gemm(const void* A, const float* a_scale, const void* Wq, const float* w_scale, const void* bias,
+                       const int32_t* cnt, const int32_t* off, const int32_t* rows, int64_t T, int K, int N, int E,
+                       int k, void* out, hipStream_t stream) {
+  const int64_t S = T * k;
+  const int64_t a_rows = GATE_UP ? T : S;
+  // 32-bit buffer offsets: the token codes and one expert's codes below 2 GiB
+  if (a_rows * K >= ((int64_t)1 << 31) || (int64_t)K * N >= ((int64_t)1 << 31)) return hipErrorNotSupported;
+  const int n_tiles = (N + kFgBN - 1) / kFgBN;
+  const int64_t m_slots = (S + kFgBM - 1) / kFgBM + E;
+  const int64_t blocks = (int64_t)n_tiles * m_slots;
+  const int64_t grid = (blocks + kXcds - 1) / kXcds * kXcds;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_fp8_kernel<GATE_UP>), dim3((unsigned)grid), dim3(kFgThreads), 0, stream,
+                     (const uint8_t*)A, a_scale, (const uint8_t*)Wq, w_scale, (const bf16_t*)bias, cnt, off, rows, K,
+                     N, E, k, (int)a_rows, n_tiles, (int)m_slots, out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fp8_quantize_rows(const void* a, int64_t R, int K, void* codes, float* scales, hipStream_t stream) {
+  if (R == 0) return hipSuccess;
+  const int64_t blocks = (R + kRowWaves - 1) / kRowWaves;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fp8_rows_kernel, dim3((unsigned)blocks), dim3(kRowWaves * kWave), 0, stream, (const bf16_t*)a, R,
+                     K, (uint8_t*)codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize_weights(const void* W, int E, int K, int N, void* codes, float* scales,
+                                       hipStream_t stream) {
+  uint32_t* amax = reinterpret_cast<uint32_t*>(scales);
+  hipLaunchKernelGGL(fp8_zero_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, amax, E);
+  const int64_t per_expert = (int64_t)K * N;
+  const int64_t nch = per_expert / 8;
+  const int gx = (int)std::min<int64_t>((nch + 255) / 256, 256);
+  hipLaunchKernelGGL(fp8_amax_kernel, dim3(gx, E), dim3(256), 0, stream, (const bf16_t*)W, per_expert, amax);
+  hipLaunchKernelGGL(fp8_weight_quant_kernel, dim3((N + kQt - 1) / kQt, (K + kQt - 1) / kQt, E), dim3(256), 0,
+                     stream, (const bf16_t*)W, K, N, (const uint32_t*)amax, (uint8_t*)codes);
+  hipLaunchKernelGGL(fp8_scale_finalize_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, amax, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8_gate_up(const void* xq, const float* sx, const void* Wq, const float* Ws, const void* bgu,
+                                   const int32_t* cnt, const int32_t* off, const int32_t* rows, int64_t T, int H,
+                                   int E, int k, int I, void* h, hipStream_t stream) {
+  return launch_gemm<true>(xq, sx, Wq, Ws, bgu, cnt, off, rows, T, H, 2 * I, E, k, h, stream);
+}
+
+hipError_t launch_gemm_fp8_down(const void* hq, const float* sh, const void* Wq, const float* Ws, const void* bd,
+                                const int32_t* cnt, const int32_t* off, int64_t T, int H, int E, int k, int I,
+                                float* o, hipStream_t stream) {
+  return launch_gemm<false>(hq, sh, Wq, Ws, bd, cnt, off, nullptr, T, I, H, E, k, o, stream);
+}
+
+}  // namespace moe

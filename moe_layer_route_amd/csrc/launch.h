@@ -52,6 +52,18 @@ hipError_t launch_gemm_mxfp4_down(const void* h, const void* Wq, const void* Ws,
                                   const int32_t* off, int64_t T, int H, int E, int k, int I, float* o,
                                   hipStream_t stream);
 
+// FP8 W8A8 (OCP E4M3): weight codes [E][N][K] with one float32 scale per
+// expert; activation codes [R][K] with one scale per row (K % 16 == 0)
+hipError_t launch_fp8_quantize_rows(const void* a, int64_t R, int K, void* codes, float* scales, hipStream_t stream);
+hipError_t launch_fp8_quantize_weights(const void* W, int E, int K, int N, void* codes, float* scales,
+                                       hipStream_t stream);
+hipError_t launch_gemm_fp8_gate_up(const void* xq, const float* sx, const void* Wq, const float* Ws, const void* bgu,
+                                   const int32_t* cnt, const int32_t* off, const int32_t* rows, int64_t T, int H,
+                                   int E, int k, int I, void* h, hipStream_t stream);
+hipError_t launch_gemm_fp8_down(const void* hq, const float* sh, const void* Wq, const float* Ws, const void* bd,
+                                const int32_t* cnt, const int32_t* off, int64_t T, int H, int E, int k, int I,
+                                float* o, hipStream_t stream);
+
 // slots with pos < 0 are left out; out_f32: y is float32 (partial sums), else bf16
 hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, int64_t T, int H, int k,
                           void* y, hipStream_t stream, bool out_f32 = false);

@@ -468,6 +468,197 @@ int moe_down_mxfp4(const void* h, const void* Wd_q, const void* Wd_s, const void
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// FP8 W8A8
+// ---------------------------------------------------------------------------
+static int check_fp8_dims(const char* fn, int32_t H, int32_t I) {
+  if (H % 16 != 0 || I % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: H=%d and I=%d must be multiples of 16 (16-byte code rows)", fn, H, I);
+  return MOE_OK;
+}
+
+struct Fp8Layout {
+  Layout base;
+  size_t xq, sx, hq, sh, total;
+};
+
+static Fp8Layout fp8_layout(int64_t T, int32_t H, int32_t E, int32_t k, int32_t I) {
+  Fp8Layout F;
+  F.base = layout(T, H, E, k, I);
+  size_t cur = F.base.total;
+  const size_t S = (size_t)T * k;
+  F.xq = take(cur, (size_t)T * H);
+  F.sx = take(cur, (size_t)T * 4);
+  F.hq = take(cur, S * I);
+  F.sh = take(cur, S * 4);
+  F.total = cur;
+  return F;
+}
+
+size_t moe_workspace_bytes_fp8(int64_t T, int32_t H, int32_t E, int32_t k, int32_t I) {
+  if (check_dims("moe_workspace_bytes_fp8", T, H, E, k, I) != MOE_OK) return 0;
+  return fp8_layout(T, H, E, k, I).total;
+}
+
+int moe_quantize_fp8(const void* W, int32_t E, int32_t K, int32_t N, void* codes, float* scales, void* stream) {
+  const char* fn = "moe_quantize_fp8";
+  if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", fn, E, MOE_MAX_E);
+  if (K < 16 || K > MOE_MAX_DIM || K % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: K=%d must be a multiple of 16 in [16, %d]", fn, K, MOE_MAX_DIM);
+  if (N < 8 || N > 2 * MOE_MAX_DIM || N % 8 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: N=%d must be a multiple of 8 in [8, %d]", fn, N, 2 * MOE_MAX_DIM);
+  CHECK_PTR(W, 16);
+  CHECK_PTR(codes, 16);
+  CHECK_PTR(scales, 4);
+  if (int st = hip_status(fn, moe::launch_fp8_quantize_weights(W, E, K, N, codes, scales, (hipStream_t)stream)))
+    return st;
+  return ok();
+}
+
+int moe_quantize_rows_fp8(const void* a, int64_t R, int32_t K, void* codes, float* scales, void* stream) {
+  const char* fn = "moe_quantize_rows_fp8";
+  if (R < 0) return fail(MOE_ERR_INVALID_ARG, "%s: R=%lld < 0", fn, (long long)R);
+  if (K < 16 || K > MOE_MAX_DIM || K % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: K=%d must be a multiple of 16 in [16, %d]", fn, K, MOE_MAX_DIM);
+  CHECK_PTR(a, 16);
+  CHECK_PTR(codes, 16);
+  CHECK_PTR(scales, 4);
+  if (int st = hip_status(fn, moe::launch_fp8_quantize_rows(a, R, K, codes, scales, (hipStream_t)stream))) return st;
+  return ok();
+}
+
+static int run_gate_up_fp8(const char* fn, const void* xq, const float* sx, const void* Wq, const float* Ws,
+                           const void* bgu, const int32_t* cnt, const int32_t* off, const int32_t* rows, int64_t T,
+                           int32_t H, int32_t E, int32_t k, int32_t I, void* h, int32_t path, hipStream_t s) {
+  path = path == MOE_PATH_AUTO ? MOE_PATH_GEMM : path;
+  if (path == MOE_PATH_GEMM)
+    return hip_status(fn, moe::launch_gemm_fp8_gate_up(xq, sx, Wq, Ws, bgu, cnt, off, rows, T, H, E, k, I, h, s));
+  if (path == MOE_PATH_GEMV) return hip_status(fn, hipErrorNotSupported);
+  return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+}
+
+static int run_down_fp8(const char* fn, const void* hq, const float* sh, const void* Wq, const float* Ws,
+                        const void* bd, const int32_t* cnt, const int32_t* off, int64_t T, int32_t H, int32_t E,
+                        int32_t k, int32_t I, float* o, int32_t path, hipStream_t s) {
+  path = path == MOE_PATH_AUTO ? MOE_PATH_GEMM : path;
+  if (path == MOE_PATH_GEMM)
+    return hip_status(fn, moe::launch_gemm_fp8_down(hq, sh, Wq, Ws, bd, cnt, off, T, H, E, k, I, o, s));
+  if (path == MOE_PATH_GEMV) return hip_status(fn, hipErrorNotSupported);
+  return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+}
+
+int moe_forward_fp8_ex(const void* x, const void* Wr, const void* br, const void* Wgu_q, const float* Wgu_s,
+                       const void* bgu, const void* Wd_q, const float* Wd_s, const void* bd, int64_t T, int32_t H,
+                       int32_t E, int32_t k, int32_t I, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                       void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
+  const char* fn = "moe_forward_fp8";
+  if (int st = check_dims(fn, T, H, E, k, I)) return st;
+  if (int st = check_fp8_dims(fn, H, I)) return st;
+  CHECK_PTR(x, 16);
+  CHECK_PTR(Wr, 16);
+  CHECK_PTR(br, 2);
+  CHECK_PTR(Wgu_q, 16);
+  CHECK_PTR(Wgu_s, 4);
+  CHECK_PTR(bgu, 4);
+  CHECK_PTR(Wd_q, 16);
+  CHECK_PTR(Wd_s, 4);
+  CHECK_PTR(bd, 4);
+  CHECK_PTR(y, 16);
+  if (topk_ids_out && !aligned(topk_ids_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_ids_out is not 4-byte aligned", fn);
+  if (topk_w_out && !aligned(topk_w_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_w_out is not 4-byte aligned", fn);
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+  if (T == 0) return ok();
+  const Fp8Layout F = fp8_layout(T, H, E, k, I);
+  if (workspace == nullptr || workspace_bytes < F.total)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, F.total);
+  if (!aligned(workspace, 256))
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+
+  char* ws = static_cast<char*>(workspace);
+  const Layout& L = F.base;
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.cnt);
+  int32_t* off = reinterpret_cast<int32_t*>(ws + L.off);
+  int32_t* rows = reinterpret_cast<int32_t*>(ws + L.rows);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+  void* h = ws + L.h;
+  float* o = reinterpret_cast<float*>(ws + L.o);
+  void* xq = ws + F.xq;
+  float* sx = reinterpret_cast<float*>(ws + F.sx);
+  void* hq = ws + F.hq;
+  float* sh = reinterpret_cast<float*>(ws + F.sh);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t S = T * k;
+
+  if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, ids, w, MOE_ROUTE_AUTO, s))) return st;
+  if (int st = hip_status(fn, moe::launch_permute(ids, T, E, k, cnt, off, rows, pos, s))) return st;
+  if (int st = hip_status(fn, moe::launch_fp8_quantize_rows(x, T, H, xq, sx, s))) return st;
+  if (int st = run_gate_up_fp8(fn, xq, sx, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, E, k, I, h, path, s)) return st;
+  if (int st = hip_status(fn, moe::launch_fp8_quantize_rows(h, S, I, hq, sh, s))) return st;
+  if (int st = run_down_fp8(fn, hq, sh, Wd_q, Wd_s, bd, cnt, off, T, H, E, k, I, o, path, s)) return st;
+  if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s))) return st;
+  return ok();
+}
+
+int moe_forward_fp8(const void* x, const void* Wr, const void* br, const void* Wgu_q, const float* Wgu_s,
+                    const void* bgu, const void* Wd_q, const float* Wd_s, const void* bd, int64_t T, int32_t H,
+                    int32_t E, int32_t k, int32_t I, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_forward_fp8_ex(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, T, H, E, k, I, y, topk_ids_out,
+                            topk_w_out, workspace, workspace_bytes, MOE_PATH_AUTO, stream);
+}
+
+int moe_gate_up_fp8(const void* xq, const float* sx, const void* Wgu_q, const float* Wgu_s, const void* bgu,
+                    const int32_t* cnt, const int32_t* off, const int32_t* rows, int64_t T, int32_t H, int32_t E,
+                    int32_t k, int32_t I, void* h, int32_t path, void* stream) {
+  const char* fn = "moe_gate_up_fp8";
+  if (int st = check_dims(fn, T, H, E, k, I)) return st;
+  if (int st = check_fp8_dims(fn, H, I)) return st;
+  CHECK_PTR(xq, 16);
+  CHECK_PTR(sx, 4);
+  CHECK_PTR(Wgu_q, 16);
+  CHECK_PTR(Wgu_s, 4);
+  CHECK_PTR(bgu, 4);
+  CHECK_PTR(cnt, 4);
+  CHECK_PTR(off, 4);
+  CHECK_PTR(rows, 4);
+  CHECK_PTR(h, 16);
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+  if (T == 0) return ok();
+  if (int st = run_gate_up_fp8(fn, xq, sx, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, E, k, I, h, path,
+                               (hipStream_t)stream))
+    return st;
+  return ok();
+}
+
+int moe_down_fp8(const void* hq, const float* sh, const void* Wd_q, const float* Wd_s, const void* bd,
+                 const int32_t* cnt, const int32_t* off, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                 float* o, int32_t path, void* stream) {
+  const char* fn = "moe_down_fp8";
+  if (int st = check_dims(fn, T, H, E, k, I)) return st;
+  if (int st = check_fp8_dims(fn, H, I)) return st;
+  CHECK_PTR(hq, 16);
+  CHECK_PTR(sh, 4);
+  CHECK_PTR(Wd_q, 16);
+  CHECK_PTR(Wd_s, 4);
+  CHECK_PTR(bd, 4);
+  CHECK_PTR(cnt, 4);
+  CHECK_PTR(off, 4);
+  CHECK_PTR(o, 16);
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+  if (T == 0) return ok();
+  if (int st = run_down_fp8(fn, hq, sh, Wd_q, Wd_s, bd, cnt, off, T, H, E, k, I, o, path, (hipStream_t)stream))
+    return st;
+  return ok();
+}
+
 int moe_combine(const float* o, const int32_t* pos, const float* topk_w, int64_t T, int32_t H, int32_t k,
                 void* y, void* stream) {
   const char* fn = "moe_combine";

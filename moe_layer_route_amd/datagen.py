@@ -27,6 +27,7 @@ import numpy as np
 
 X_ID, WR_ID, BR_ID, WGU_ID, BGU_ID, WD_ID, BD_ID, PERM_ID = 1, 2, 3, 4, 5, 6, 7, 8
 MXGU_ID, MXD_ID = 9, 10
+F8GU_ID, F8D_ID, F8S_ID = 11, 12, 13
 
 # Scale of x that puts about 5% of the gate/up pre-activations past the +-7
 # clamp for weights N(0, 0.02) and biases N(0, 0.01) at H = 2880: a
@@ -265,6 +266,67 @@ def make_experts_mxfp4(cfg: MoEConfig, seed: int = 0, threads: int | None = None
     def one(e):
         gq[e], gs[e] = mxfp4_draw(2 * I, H, seed, MXGU_ID, E, e)
         dq[e], ds[e] = mxfp4_draw(H, I, seed, MXD_ID, E, e)
+        bgu[e] = normal_bf16((2 * I,), BIAS_STD, seed, BGU_ID, E, e)
+        bd[e] = normal_bf16((H,), BIAS_STD, seed, BD_ID, E, e)
+
+    if threads is None:
+        threads = min(16, max(1, len(_affinity())))
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(one, range(E)))
+    return gq, gs, bgu, dq, ds, bd
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) expert weights, drawn directly.  A code is sign | exponent field
+# << 3 | mantissa field: the exponent field follows FP8_EXP_FREQ, the share
+# of each binade among N(0, sigma) weights whose expert maximum (about 5.5
+# sigma) is scaled to 448; mantissa and sign are uniform (the top binade
+# excludes mantissa 7, the NaN pattern).  One float32 scale per expert near
+# 5.5 * 0.02 / 448.
+# ---------------------------------------------------------------------------
+FP8_EXP_FREQ = (0.0002, 0.0002, 0.0003, 0.0006, 0.0012, 0.0025, 0.0049, 0.0098,
+                0.0196, 0.039, 0.075, 0.150, 0.262, 0.316, 0.115, 0.002)
+FP8_SCALE_MEAN = 5.5 * 0.02 / 448.0
+
+_F8 = None
+
+
+def _fp8_table():
+    """65536-entry table: a uniform 16-bit draw -> one code."""
+    p = np.zeros(256)
+    for ex, f in enumerate(FP8_EXP_FREQ):
+        mants = 7 if ex == 15 else 8
+        for m in range(mants):
+            p[(ex << 3) | m] = f / mants / 2.0
+            p[0x80 | (ex << 3) | m] = f / mants / 2.0
+    edges = np.cumsum(p) / p.sum() * 65536.0
+    return np.minimum(np.searchsorted(edges, np.arange(65536) + 0.5), 255).astype(np.uint8)
+
+
+def fp8_draw(N: int, K: int, seed: int, tensor_id: int, a: int, b: int) -> np.ndarray:
+    """codes uint8 [N][K] from the (tensor_id, a, b) stream."""
+    global _F8
+    if _F8 is None:
+        _F8 = _fp8_table()
+    return _F8[_rng(seed, tensor_id, a, b).integers(0, 65536, size=(N, K), dtype=np.uint16)]
+
+
+def make_experts_fp8(cfg: MoEConfig, seed: int = 0, threads: int | None = None):
+    """FP8 expert weights: gate_up codes [E][2I][H] and scales [E], down codes
+    [E][H][I] and scales [E] (codes K-contiguous), one stream per (tensor,
+    expert).  The biases are those of make_experts."""
+    E, H, I = cfg.E, cfg.H, cfg.I
+    gq = np.empty((E, 2 * I, H), np.uint8)
+    dq = np.empty((E, H, I), np.uint8)
+    bgu = np.empty((E, 2 * I), dtype=np.uint16)
+    bd = np.empty((E, H), dtype=np.uint16)
+    g = _rng(seed, F8S_ID, E, 0)
+    gs = (FP8_SCALE_MEAN * (1.0 + 0.05 * g.standard_normal(E))).astype(np.float32)
+    ds = (FP8_SCALE_MEAN * (1.0 + 0.05 * g.standard_normal(E))).astype(np.float32)
+
+    def one(e):
+        gq[e] = fp8_draw(2 * I, H, seed, F8GU_ID, E, e)
+        dq[e] = fp8_draw(H, I, seed, F8D_ID, E, e)
         bgu[e] = normal_bf16((2 * I,), BIAS_STD, seed, BGU_ID, E, e)
         bd[e] = normal_bf16((H,), BIAS_STD, seed, BD_ID, E, e)
 

@@ -175,3 +175,38 @@ def test_mxfp4_calls_validate(lib):
     assert lib.moe_quantize_mxfp4(v, 0, 64, 64, v, v, None) == INVALID
     assert lib.moe_quantize_mxfp4(v, 4, 64, 64, ctypes.c_void_p(FAKE + 8), v, None) == INVALID
     assert b"aligned" in lib.moe_last_error()
+
+
+def _fwd_fp8(lib, T=4, H=64, E=8, k=2, I=64, ptrs=None, ws_bytes=1 << 30, path=0):
+    vp = [ctypes.c_void_p(p) for p in (ptrs or [FAKE] * 10)]
+    return lib.moe_forward_fp8_ex(*vp[:9], T, H, E, k, I, vp[9], None, None, ctypes.c_void_p(FAKE), ws_bytes, path,
+                                  None)
+
+
+def test_fp8_calls_validate(lib):
+    v = ctypes.c_void_p(FAKE)
+    # H and I must be multiples of 16 (16-byte code rows)
+    assert _fwd_fp8(lib, H=40) == INVALID and b"multiples of 16" in lib.moe_last_error()
+    assert _fwd_fp8(lib, I=24) == INVALID
+    for i in range(10):
+        p = [FAKE] * 10
+        p[i] = 0
+        assert _fwd_fp8(lib, ptrs=p) == INVALID
+        assert b"is NULL" in lib.moe_last_error()
+    need = lib.moe_workspace_bytes_fp8(4, 64, 8, 2, 64)
+    assert need > lib.moe_workspace_bytes(4, 64, 8, 2, 64)
+    assert _fwd_fp8(lib, ws_bytes=need - 1) == WORKSPACE
+    assert _fwd_fp8(lib, T=0) == OK
+    assert _fwd_fp8(lib, path=7) == INVALID and b"unknown path" in lib.moe_last_error()
+    assert lib.moe_gate_up_fp8(v, v, v, v, v, v, v, v, 4, 72, 8, 2, 64, v, 0, None) == INVALID
+    assert lib.moe_down_fp8(v, None, v, v, v, v, v, 4, 64, 8, 2, 64, v, 0, None) == INVALID
+    assert lib.moe_gate_up_fp8(v, v, v, v, v, v, v, v, 4, 64, 8, 2, 64, v, 3, None) == INVALID
+    # the quantisers: K % 16 == 0, N % 8 == 0, codes 16-byte aligned
+    assert lib.moe_quantize_fp8(v, 4, 40, 64, v, v, None) == INVALID and b"K=40" in lib.moe_last_error()
+    assert lib.moe_quantize_fp8(v, 4, 64, 12, v, v, None) == INVALID and b"N=12" in lib.moe_last_error()
+    assert lib.moe_quantize_fp8(v, 0, 64, 64, v, v, None) == INVALID
+    assert lib.moe_quantize_fp8(v, 4, 64, 64, ctypes.c_void_p(FAKE + 8), v, None) == INVALID
+    assert lib.moe_quantize_rows_fp8(v, -1, 64, v, v, None) == INVALID
+    assert lib.moe_quantize_rows_fp8(v, 4, 24, v, v, None) == INVALID and b"K=24" in lib.moe_last_error()
+    assert lib.moe_quantize_rows_fp8(v, 4, 64, v, ctypes.c_void_p(FAKE + 2), None) == INVALID
+    assert lib.moe_workspace_bytes_fp8(4, 64, 0, 2, 64) == 0
