@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 METRIC = "MoE-layer tokens/sec + % of HBM or bf16 MFMA roofline on 1 MI355X"
 
 
@@ -65,6 +66,22 @@ def _alg_bytes_layer_mxfp4(cfg, D):
 def _alg_bytes_gate_up_mxfp4(cfg, D):
     H, I, T, k = cfg.H, cfg.I, cfg.T, cfg.k
     return D * (_mx_bytes(H, 2 * I) + 2 * I * 2) + T * H * 2 + T * k * I * 2
+
+
+def _f8_bytes(K, N):
+    """One FP8 weight [N][K]: one byte per value plus its float32 scale."""
+    return N * K + 4
+
+
+def _alg_bytes_layer_fp8(cfg, D):
+    H, I, E, T = cfg.H, cfg.I, cfg.E, cfg.T
+    per_expert = _f8_bytes(H, 2 * I) + _f8_bytes(I, H) + 2 * I * 2 + H * 2
+    return D * per_expert + E * H * 2 + E * 2 + 2 * T * H * 2
+
+
+def _alg_bytes_gate_up_fp8(cfg, D):
+    H, I, T, k = cfg.H, cfg.I, cfg.T, cfg.k
+    return D * (_f8_bytes(H, 2 * I) + 2 * I * 2) + T * H * 2 + T * k * I * 2
 
 
 def _alg_flops_layer(cfg):
@@ -99,10 +116,11 @@ def _traffic(kernel_file, workload, launches_bytes_unit=1.0):
         return None
 
 
-def cpu_baseline(inp, k, min_seconds=10.0, max_reps=3, mx_arrays=None):
+def cpu_baseline(inp, k, min_seconds=10.0, max_reps=3, mx_arrays=None, f8_arrays=None):
     """The float64 oracle on the host cores over the whole workload, repeated
-    until about min_seconds of CPU time (at most max_reps runs).  mx_arrays:
-    the MXFP4 inputs, timed through the oracle's MXFP4 forward instead."""
+    until about min_seconds of CPU time (at most max_reps runs).  mx_arrays /
+    f8_arrays: the MXFP4 or FP8 inputs, timed through the oracle's forward for
+    that format instead."""
     import numpy as np
     import oracle.moe_oracle as orc
     try:
@@ -114,15 +132,18 @@ def cpu_baseline(inp, k, min_seconds=10.0, max_reps=3, mx_arrays=None):
     t_all = time.perf_counter()
     while len(times) < max_reps and (time.perf_counter() - t_all) < min_seconds:
         t0 = time.perf_counter()
-        if mx_arrays is None:
-            orc.moe_forward(*inp.arrays(), k=k)
-        else:
+        if mx_arrays is not None:
             orc.moe_forward_mxfp4(*mx_arrays, k=k)
+        elif f8_arrays is not None:
+            orc.moe_forward_fp8(*f8_arrays, k=k)
+        else:
+            orc.moe_forward(*inp.arrays(), k=k)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     return {"value": inp.cfg.T / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"whole {inp.cfg.name} batch (T={inp.cfg.T}) through the float64 numpy oracle"
-                      f"{' (MXFP4 weights)' if mx_arrays is not None else ''}, "
+                      f"{' (MXFP4 weights)' if mx_arrays is not None else ''}"
+                      f"{' (FP8 W8A8)' if f8_arrays is not None else ''}, "
                       f"median of {len(times)} runs of {t:.2f} s"}
 
 
@@ -181,8 +202,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
-    ap.add_argument("--weights", default="bf16", choices=["bf16", "mxfp4"],
-                    help="expert weight format: bf16 (moe_forward) or MXFP4 W4A16 (moe_forward_mxfp4)")
+    ap.add_argument("--weights", default="bf16", choices=["bf16", "mxfp4", "fp8"],
+                    help="expert weight format: bf16 (moe_forward), MXFP4 W4A16 (moe_forward_mxfp4) or FP8 "
+                         "W8A8 (moe_forward_fp8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ep", type=int, default=1,
                     help="also time one expert-parallel rank's share of W ranks: experts [0, E/W), "
@@ -221,7 +243,18 @@ def main(argv=None):
 
     x, Wr, br, Wgu, bgu, Wd, bd = [dev(a) for a in inp.arrays()]
     mx = args.weights == "mxfp4"
-    mx_arrays = None
+    f8 = args.weights == "fp8"
+    mx_arrays = f8_arrays = None
+    if (mx or f8) and args.ep > 1:
+        print("bench.py: --ep is measured with bf16 weights only", file=sys.stderr)
+        return 2
+    if f8:
+        gq, gs, bgu_f, dq, ds, bd_f = d.make_experts_fp8(cfg, seed=0)
+        f8_arrays = (inp.x, inp.Wr, inp.br, gq, gs, bgu_f, dq, ds, bd_f)
+        Wgu_q, Wgu_s, Wd_q, Wd_s = [torch.from_numpy(a).cuda() for a in (gq, gs, dq, ds)]
+        bgu, bd = dev(bgu_f), dev(bd_f)
+        del Wgu, Wd
+        print("[bench] FP8 expert weights ready", file=sys.stderr, flush=True)
     if mx:
         if args.ep > 1:
             print("bench.py: --ep is measured with bf16 weights only", file=sys.stderr)
@@ -233,14 +266,18 @@ def main(argv=None):
         del Wgu, Wd
         print("[bench] MXFP4 expert weights ready", file=sys.stderr, flush=True)
     T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
-    ws = binding.alloc_workspace(T, H, E, k, I)
+    ws = binding.alloc_workspace_fp8(T, H, E, k, I) if f8 else binding.alloc_workspace(T, H, E, k, I)
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(st=None):
-        if mx:
+        if f8:
+            binding.moe_forward_fp8(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k=k, y=y, workspace=ws,
+                                    topk_ids=ids, topk_w=w, path=args.path,
+                                    stream=st if st is not None else stream)
+        elif mx:
             binding.moe_forward_mxfp4(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k=k, y=y, workspace=ws,
                                       topk_ids=ids, topk_w=w, path=args.path,
                                       stream=st if st is not None else stream)
@@ -297,21 +334,33 @@ def main(argv=None):
     h = torch.empty((T * k, I), dtype=torch.bfloat16, device="cuda")
     o = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    if f8:
+        xq = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+        sx = torch.empty((T,), dtype=torch.float32, device="cuda")
+        hq = torch.empty((T * k, I), dtype=torch.uint8, device="cuda")
+        sh = torch.empty((T * k,), dtype=torch.float32, device="cuda")
 
     def stage_step(ev=None):
         binding.moe_route(x, Wr, br, k, topk_ids=ids, topk_w=w, stream=stream)
         st = binding.library().moe_permute(binding._ptr(ids), T, E, k, binding._ptr(cnt), binding._ptr(off),
                                            binding._ptr(rows), binding._ptr(pos), binding._stream(stream))
         binding._check(st, "moe_permute")
+        if f8:
+            binding.moe_quantize_rows_fp8(x, codes=xq, scales=sx, stream=stream)
         if ev:
             ev[0].record(stream)
-        if mx:
+        if f8:
+            binding.moe_gate_up_fp8(xq, sx, Wgu_q, Wgu_s, bgu, cnt, off, rows, k, h=h, path=args.path, stream=stream)
+        elif mx:
             binding.moe_gate_up_mxfp4(x, Wgu_q, Wgu_s, bgu, cnt, off, rows, k, h=h, path=args.path, stream=stream)
         else:
             binding.moe_gate_up(x, Wgu, bgu, cnt, off, rows, k, path=args.path, h=h, stream=stream)
         if ev:
             ev[1].record(stream)
-        if mx:
+        if f8:
+            binding.moe_quantize_rows_fp8(h, codes=hq, scales=sh, stream=stream)
+            binding.moe_down_fp8(hq, sh, Wd_q, Wd_s, bd, cnt, off, T, k, o=o, path=args.path, stream=stream)
+        elif mx:
             binding.moe_down_mxfp4(h, Wd_q, Wd_s, bd, cnt, off, T, k, o=o, path=args.path, stream=stream)
         else:
             binding.moe_down(h, Wd, bd, cnt, off, T, k, path=args.path, o=o, stream=stream)
@@ -326,13 +375,18 @@ def main(argv=None):
     gate_up_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     D = int((torch.bincount(ids.reshape(-1).long(), minlength=E) > 0).sum().item())
-    path = args.path if args.path != "auto" else binding.expert_path(T, E, k)
-    gu_bytes = _alg_bytes_gate_up_mxfp4(cfg, D) if mx else _alg_bytes_gate_up(cfg, D)
+    path = args.path if args.path != "auto" else ("gemm" if f8 else binding.expert_path(T, E, k))
+    gu_bytes = (_alg_bytes_gate_up_mxfp4(cfg, D) if mx else _alg_bytes_gate_up_fp8(cfg, D) if f8
+                else _alg_bytes_gate_up(cfg, D))
     gu_flops = 2 * T * k * H * 2 * I
-    gu_file = f"moe_layer_route_amd/csrc/{'mxfp4' if path == 'gemv' else 'mxfp4_gemm'}.hip" if mx else \
-        f"moe_layer_route_amd/csrc/{path}.hip"
+    gu_file = (f"moe_layer_route_amd/csrc/{'mxfp4' if path == 'gemv' else 'mxfp4_gemm'}.hip" if mx else
+               "moe_layer_route_amd/csrc/fp8.hip" if f8 else f"moe_layer_route_amd/csrc/{path}.hip")
     traffic = _traffic(gu_file, cfg.name)
-    if mx and path == "gemv":
+    if f8:
+        roofline = {"bound": "mfma", "kernel": "gemm_fp8_kernel<gate_up>",
+                    "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12, "peak": FP8_PEAK_TFLOPS,
+                    "unit": "TFLOP/s"}
+    elif mx and path == "gemv":
         roofline = {"bound": "hbm", "kernel": "gemv_mxfp4_kernel<gate_up>",
                     "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     elif mx:
@@ -348,7 +402,9 @@ def main(argv=None):
                     "unit": "TFLOP/s"}
     roofline.update(frac=roofline["achieved"] / roofline["peak"], traffic=traffic,
                     alg_bytes_per_launch=gu_bytes, alg_flops_per_launch=gu_flops, launch_us=gate_up_ms * 1e3)
-    layer_bytes = _alg_bytes_layer_mxfp4(cfg, D) if mx else _alg_bytes_layer(cfg, D)
+    layer_bytes = (_alg_bytes_layer_mxfp4(cfg, D) if mx else _alg_bytes_layer_fp8(cfg, D) if f8
+                   else _alg_bytes_layer(cfg, D))
+    mfma_peak = FP8_PEAK_TFLOPS if f8 else BF16_PEAK_TFLOPS
     layer_flops = _alg_flops_layer(cfg)
     step_s = ms_per_step * 1e-3
 
@@ -393,7 +449,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if f8 else "bf16",
         "data": "synthetic (seeded normal bf16 inputs of the gpt-oss MoE block shapes; random-init weights)",
         "config": {"workload": f"{cfg.name}: {cfg.description}", "T": T, "H": H, "I": I, "E": E, "k": k,
                    "seed": 0, "path": path, "live_experts": D, "weights": args.weights},
@@ -401,7 +457,7 @@ def main(argv=None):
         "layer": {"alg_bytes": layer_bytes, "alg_flops": layer_flops,
                   "hbm_GBs": layer_bytes / step_s / 1e9, "hbm_frac": layer_bytes / step_s / 1e9 / HBM_PEAK_GBS,
                   "tflops": layer_flops / step_s / 1e12,
-                  "mfma_frac": layer_flops / step_s / 1e12 / BF16_PEAK_TFLOPS},
+                  "mfma_frac": layer_flops / step_s / 1e12 / mfma_peak},
         "latency_us": lat,
         "cold_latency_us": cold,
         "graph_ms_per_step": graph_ms,
@@ -411,7 +467,7 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp, k, mx_arrays=mx_arrays)
+        out["cpu_baseline"] = cpu_baseline(inp, k, mx_arrays=mx_arrays, f8_arrays=f8_arrays)
     print(json.dumps(out), flush=True)
     return 0
 

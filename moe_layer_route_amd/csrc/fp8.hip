@@ -26,9 +26,10 @@
 //   steps ahead in a ring of two register sets, copied out at the step start
 //   so the set can be reloaded at once.
 //   A (codes of token rows): gathered through rows[] (gate_up) or contiguous
-//   (down), two 16-byte pieces per thread three steps ahead, stored into the
-//   fragment-major LDS ring two steps ahead: fragment mi (rows 32mi..32mi+31)
-//   holds, in lane order, the 32 bytes lane l of the MFMA needs.
+//   (down), two 16-byte pieces per thread four steps ahead, stored into the
+//   fragment-major LDS ring two steps ahead (so each load has two steps to
+//   arrive): fragment mi (rows 32mi..32mi+31) holds, in lane order, the 32
+//   bytes lane l of the MFMA needs.
 // Epilogue: in the 32 x 32 accumulator layout lane l, element v holds row
 // 8*(v/4) + 4*(l/32) + v%4 of MFMA column l%32, i.e. weight column
 // n0 + 128w + 4c + j of block j: a lane holds two whole (gate, up) pairs.
@@ -352,14 +353,15 @@ __global__ __launch_bounds__(kFgThreads, 1) void gemm_fp8_kernel(
 
   // Registers (the loop is unrolled three times and no ring needs a register
   // copy): B of steps kt, kt+1, kt+2 (Rb[kt%3] is used by step kt and then
-  // reloaded, at step kt+1, with step kt+3), A of steps kt+2 and kt+3 (Ra,
-  // same ring), the A fragments F of step kt (each reloaded with step kt+1
-  // after its last MFMA).
+  // reloaded, at step kt+1, with step kt+3), A of steps kt+2, kt+3 and kt+4
+  // (Ra[j%3] holds A(j) from its load, four steps ahead, to its LDS store,
+  // two steps ahead), the A fragments F of step kt (each reloaded with step
+  // kt+1 after its last MFMA).
   u32x4_t Rb[3][4][2];
   u32x4_t Ra[3][2];
   u32x4_t F[4][2];
 
-  // One K step kt (r = kt % 3): issue the loads of A(kt+3), then B(kt+2)
+  // One K step kt (r = kt % 3): issue the loads of A(kt+4), then B(kt+2)
   // (loads retire in order: the next step's store of A waits for A alone);
   // multiply B(kt) with F, reading the fragments of kt+1 as those of kt
   // retire; store A(kt+2); one barrier after the third of the four MFMA
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(kFgThreads, 1) void gemm_fp8_kernel(
     constexpr int r = decltype(rc)::value;
     const u32x4_t (&bt)[4][2] = Rb[r];
     __builtin_amdgcn_sched_barrier(0);
-    gload_a(kt + 3, Ra[r]);
+    gload_a(kt + 4, Ra[(r + 1) % 3]);
     gload_b(kt + 2, Rb[(r + 2) % 3]);
     const int nbuf = (kt + 1) % kFgLdsBufs;
     auto group = [&](int mi) {
@@ -407,14 +409,15 @@ __global__ __launch_bounds__(kFgThreads, 1) void gemm_fp8_kernel(
     lread(nbuf, 3, F[3]);
   };
 
-  // Prologue: the loads in the order the steps issue them (A(j+1), then
+  // Prologue: the loads in the order the steps issue them (A(j+2), then
   // B(j)), so the wait counts of the first steps match the later ones.
   const int nk = (K + kFgBK - 1) / kFgBK;
   gload_a(0, Ra[0]);
   gload_a(1, Ra[1]);
+  gload_a(2, Ra[2]);
   gload_b(0, Rb[0]);
   lstore(0, Ra[0]);
-  gload_a(2, Ra[2]);
+  gload_a(3, Ra[0]);
   gload_b(1, Rb[1]);
   lstore(1, Ra[1]);
   __syncthreads();
