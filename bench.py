@@ -97,10 +97,12 @@ def _source_digest(files):
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel_file, workload, launches_bytes_unit=1.0):
+def _traffic(kernel_file, workload, stem=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when there is none or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"counters_{kernel_file.split('/')[-1].split('.')[0]}_{workload}.txt")
+    None when there is none or the kernel source changed since it was taken.
+    stem names the summary when one source file holds several kernels."""
+    stem = stem or kernel_file.split('/')[-1].split('.')[0]
+    path = os.path.join(ROOT, "profiles", f"counters_{stem}_{workload}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -375,14 +377,18 @@ def main(argv=None):
     gate_up_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     D = int((torch.bincount(ids.reshape(-1).long(), minlength=E) > 0).sum().item())
-    path = args.path if args.path != "auto" else ("gemm" if f8 else binding.expert_path(T, E, k))
+    path = args.path if args.path != "auto" else binding.expert_path(T, E, k)
     gu_bytes = (_alg_bytes_gate_up_mxfp4(cfg, D) if mx else _alg_bytes_gate_up_fp8(cfg, D) if f8
                 else _alg_bytes_gate_up(cfg, D))
     gu_flops = 2 * T * k * H * 2 * I
     gu_file = (f"moe_layer_route_amd/csrc/{'mxfp4' if path == 'gemv' else 'mxfp4_gemm'}.hip" if mx else
                "moe_layer_route_amd/csrc/fp8.hip" if f8 else f"moe_layer_route_amd/csrc/{path}.hip")
-    traffic = _traffic(gu_file, cfg.name)
-    if f8:
+    gu_stem = "fp8_gemv" if f8 and path == "gemv" else "fp8_gemm" if f8 else None
+    traffic = _traffic(gu_file, cfg.name, stem=gu_stem)
+    if f8 and path == "gemv":
+        roofline = {"bound": "hbm", "kernel": "gemv_fp8_kernel<gate_up>",
+                    "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    elif f8:
         roofline = {"bound": "mfma", "kernel": "gemm_fp8_kernel<gate_up>",
                     "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12, "peak": FP8_PEAK_TFLOPS,
                     "unit": "TFLOP/s"}

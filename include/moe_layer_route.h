@@ -371,9 +371,10 @@ MOE_API size_t moe_workspace_bytes_fp8(int64_t T, int32_t H, int32_t E, int32_t 
  *   Wd_q  uint8 [E][H][I],  Wd_s  float32 [E]   down
  * x is quantised per token and h per (token, slot) row on the device, inside
  * the call.  Every other argument and output is as in moe_forward; the
- * workspace must hold moe_workspace_bytes_fp8(...) bytes.  Expert paths:
- * MOE_PATH_GEMM is the LDS-tiled grouped GEMM on the FP8 matrix cores;
- * MOE_PATH_GEMV returns MOE_ERR_UNSUPPORTED; AUTO takes MOE_PATH_GEMM.
+ * workspace must hold moe_workspace_bytes_fp8(...) bytes.  Expert paths, both
+ * on the FP8 matrix cores: MOE_PATH_GEMV streams the 8-bit weights (one pass
+ * over each live expert's weights per 32 rows), MOE_PATH_GEMM is the
+ * LDS-tiled grouped GEMM; AUTO picks from T*k/E as moe_expert_path does.
  */
 MOE_API int moe_forward_fp8(const void* x, const void* Wr, const void* br,
                             const void* Wgu_q, const float* Wgu_s, const void* bgu,

@@ -488,6 +488,193 @@ hipError_t launch_gemm(const void* A, const float* a_scale, const void* Wq, cons
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming kernel (few rows per expert): one wave per workgroup, one
+// expert x 64 output columns over the whole of K (no K split, no LDS, no
+// barrier), v_mfma_f32_16x16x128_f8f6f4 on K steps of 128 codes.
+//   K slots: operand byte q of lane group g (g = lane/16) is K = 64*(q/16) +
+//   16g + q%16 of the step, so lane (c = lane%16, g)'s two 16-byte pieces of
+//   a column, together with the other three groups', read the column's 128
+//   codes as two contiguous 64-byte runs.
+//   Call j = 0..3 takes column n0 + 4c + j (a lane holds two whole (gate, up)
+//   pairs); the token operand is 16 rows of x (or h) codes gathered in the
+//   same K order.  Weight loads run two steps ahead in a ring of three
+//   register sets (32 bytes per lane and column a step: a deeper ring would
+//   leave one wave per SIMD), token rows (L2-resident) one step ahead.
+// ---------------------------------------------------------------------------
+constexpr int kF8NJ = 4;                 // columns per lane
+constexpr int kF8Cols = 16 * kF8NJ;      // 64 columns per wave
+constexpr int kF8BK = 128;               // codes per K step
+
+struct F8W {
+  u32x4_t w[kF8NJ][2];
+};
+template <int MG>
+struct F8A {
+  u32x4_t a[MG][2];
+};
+
+__device__ __forceinline__ f32x4_t mfma_fp8_16(const u32x4_t (&a)[2], const u32x4_t (&b)[2], f32x4_t c) {
+  const i32x8_t av = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
+                      (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+  const i32x8_t bv = {(int)b[0].x, (int)b[0].y, (int)b[0].z, (int)b[0].w,
+                      (int)b[1].x, (int)b[1].y, (int)b[1].z, (int)b[1].w};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <bool GATE_UP, int MG>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 2 : 1))) void gemv_fp8_kernel(
+    const uint8_t* __restrict__ A,        // gate_up: x codes [T][K]; down: h codes [S][K] (permuted order)
+    const float* __restrict__ a_scale,    // gate_up: [T]; down: [S]
+    const uint8_t* __restrict__ Wq,       // [E][N][K]
+    const float* __restrict__ w_scale,    // [E]
+    const bf16_t* __restrict__ bias,      // [E][N]
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ rows,     // gate_up only: permuted slot ids
+    int K, int N, int kslots, int a_rows, void* __restrict__ out) {
+  const int e = blockIdx.y;
+  const int M = cnt[e];
+  if (M == 0) return;   // the whole (one-wave) workgroup: no load for an expert without rows
+  const int row0 = off[e];
+  const int lane = threadIdx.x;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  // N % 4 == 0 and ncol % 4 == 0: a lane's four columns are all in range or all out
+  const int ncol = blockIdx.x * kF8Cols + kF8NJ * c;
+  const bool col_ok = ncol < N;
+
+  const rsrc_t w_rs = make_rsrc(Wq + (size_t)e * N * K, (uint32_t)N * (uint32_t)K);
+  const rsrc_t a_rs = make_rsrc(A, (uint32_t)((size_t)a_rows * K));
+  uint32_t w_off[kF8NJ];
+#pragma unroll
+  for (int j = 0; j < kF8NJ; ++j) w_off[j] = (uint32_t)min(ncol + j, N - 1) * (uint32_t)K + 16u * g;
+  const int nk = (K + kF8BK - 1) / kF8BK;
+  const float ws = w_scale[e];
+
+  for (int r0 = 0; r0 < M; r0 += 16 * MG) {
+    const int nch = min(MG, (M - r0 + 15) / 16);   // uniform
+    uint32_t a_off[MG];
+#pragma unroll
+    for (int qq = 0; qq < MG; ++qq) {
+      const int m = min(r0 + 16 * qq + c, M - 1);   // A row of this lane (clamped)
+      const uint32_t r = GATE_UP ? (uint32_t)(rows[row0 + m] / kslots) : (uint32_t)(row0 + m);
+      a_off[qq] = r * (uint32_t)K + 16u * g;
+    }
+    f32x4_t acc[MG][kF8NJ];
+#pragma unroll
+    for (int qq = 0; qq < MG; ++qq)
+#pragma unroll
+      for (int j = 0; j < kF8NJ; ++j) acc[qq][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // loads of step q; pieces past K read 0 (sent outside the descriptors)
+    auto load_w = [&](int q, F8W& d) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t kb = (uint32_t)(q * kF8BK + 64 * h);
+        const bool in = (int)kb + 16 * g < K;
+#pragma unroll
+        for (int j = 0; j < kF8NJ; ++j) d.w[j][h] = buf_ld16(w_rs, in ? w_off[j] + kb : kOutOfRange);
+      }
+    };
+    auto load_a = [&](int q, F8A<MG>& d) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t kb = (uint32_t)(q * kF8BK + 64 * h);
+        const bool in = (int)kb + 16 * g < K;
+#pragma unroll
+        for (int qq = 0; qq < MG; ++qq) d.a[qq][h] = buf_ld16(a_rs, in ? a_off[qq] + kb : kOutOfRange);
+      }
+    };
+    auto step = [&](const F8W& dw, const F8A<MG>& da) {
+#pragma unroll
+      for (int j = 0; j < kF8NJ; ++j) {
+        acc[0][j] = mfma_fp8_16(da.a[0], dw.w[j], acc[0][j]);
+        if (MG > 1 && nch > 1) {
+#pragma unroll
+          for (int qq = 1; qq < MG; ++qq) acc[qq][j] = mfma_fp8_16(da.a[qq], dw.w[j], acc[qq][j]);
+        }
+      }
+    };
+
+    F8W w0, w1, w2;
+    F8A<MG> a0, a1, a2;
+    load_w(0, w0);
+    load_w(1, w1);
+    load_a(0, a0);
+    int q = 0;
+    for (; q + 3 <= nk; q += 3) {
+      load_w(q + 2, w2);
+      load_a(q + 1, a1);
+      step(w0, a0);
+      load_w(q + 3, w0);
+      load_a(q + 2, a2);
+      step(w1, a1);
+      load_w(q + 4, w1);
+      load_a(q + 3, a0);
+      step(w2, a2);
+    }
+    // 0..2 steps left; w0, w1 hold steps q, q+1 and a0 holds step q
+    if (q < nk) {
+      load_a(q + 1, a1);
+      step(w0, a0);
+    }
+    if (q + 1 < nk) step(w1, a1);
+
+    // epilogue: 16x16 accumulator layout, lane (c, g) element v holds row
+    // 4g + v of MFMA column c = weight column ncol + j of call j
+    if (col_ok) {
+      float bb[kF8NJ];
+      {
+        const uint32_t* bp = reinterpret_cast<const uint32_t*>(bias + (size_t)e * N + ncol);
+        const uint32_t b01 = bp[0], b23 = bp[1];
+        bb[0] = bf16lo(b01);
+        bb[1] = bf16hi(b01);
+        bb[2] = bf16lo(b23);
+        bb[3] = bf16hi(b23);
+      }
+#pragma unroll
+      for (int qq = 0; qq < MG; ++qq) {
+        if (qq < nch) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int m = r0 + 16 * qq + 4 * g + v;
+            if (m < M) {
+              const size_t orow = (size_t)(row0 + m);
+              const float sc = (GATE_UP ? a_scale[rows[row0 + m] / kslots] : a_scale[orow]) * ws;
+              if (GATE_UP) {
+                const float h0 = clamped_glu(acc[qq][0][v] * sc + bb[0], acc[qq][1][v] * sc + bb[1]);
+                const float h1 = clamped_glu(acc[qq][2][v] * sc + bb[2], acc[qq][3][v] * sc + bb[3]);
+                *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + orow * (N / 2) + ncol / 2) =
+                    pack_bf16x2(h0, h1);
+              } else {
+                *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + orow * N + ncol) =
+                    f32x4_t{acc[qq][0][v] * sc + bb[0], acc[qq][1][v] * sc + bb[1], acc[qq][2][v] * sc + bb[2],
+                            acc[qq][3][v] * sc + bb[3]};
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool GATE_UP>
+hipError_t launch_gemv(const void* A, const float* a_scale, const void* Wq, const float* w_scale, const void* bias,
+                       const int32_t* cnt, const int32_t* off, const int32_t* rows, int64_t T, int K, int N, int E,
+                       int k, void* out, hipStream_t stream) {
+  const int64_t S = T * k;
+  const int64_t a_rows = GATE_UP ? T : S;
+  if (a_rows * K >= ((int64_t)1 << 31) || (int64_t)K * N >= ((int64_t)1 << 31)) return hipErrorNotSupported;
+  const dim3 grid((N + kF8Cols - 1) / kF8Cols, E);
+  // 32 rows per pass once the mean load per expert passes 10 rows
+  const bool one = S <= 10 * (int64_t)E;
+  auto kern = one ? gemv_fp8_kernel<GATE_UP, 1> : gemv_fp8_kernel<GATE_UP, 2>;
+  hipLaunchKernelGGL(kern, grid, dim3(kWave), 0, stream, (const uint8_t*)A, a_scale, (const uint8_t*)Wq, w_scale,
+                     (const bf16_t*)bias, cnt, off, rows, K, N, GATE_UP ? k : 1, (int)a_rows, out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fp8_quantize_rows(const void* a, int64_t R, int K, void* codes, float* scales, hipStream_t stream) {
@@ -525,4 +712,18 @@ hipError_t launch_gemm_fp8_down(const void* hq, const float* sh, const void* Wq,
   return launch_gemm<false>(hq, sh, Wq, Ws, bd, cnt, off, nullptr, T, I, H, E, k, o, stream);
 }
 
+}  // namespace moe
+
+namespace moe {
+hipError_t launch_gemv_fp8_gate_up(const void* xq, const float* sx, const void* Wq, const float* Ws, const void* bgu,
+                                   const int32_t* cnt, const int32_t* off, const int32_t* rows, int64_t T, int H,
+                                   int E, int k, int I, void* h, hipStream_t stream) {
+  return launch_gemv<true>(xq, sx, Wq, Ws, bgu, cnt, off, rows, T, H, 2 * I, E, k, h, stream);
+}
+
+hipError_t launch_gemv_fp8_down(const void* hq, const float* sh, const void* Wq, const float* Ws, const void* bd,
+                                const int32_t* cnt, const int32_t* off, int64_t T, int H, int E, int k, int I,
+                                float* o, hipStream_t stream) {
+  return launch_gemv<false>(hq, sh, Wq, Ws, bd, cnt, off, nullptr, T, I, H, E, k, o, stream);
+}
 }  // namespace moe

@@ -63,6 +63,12 @@ hipError_t launch_gemm_fp8_gate_up(const void* xq, const float* sx, const void* 
 hipError_t launch_gemm_fp8_down(const void* hq, const float* sh, const void* Wq, const float* Ws, const void* bd,
                                 const int32_t* cnt, const int32_t* off, int64_t T, int H, int E, int k, int I,
                                 float* o, hipStream_t stream);
+hipError_t launch_gemv_fp8_gate_up(const void* xq, const float* sx, const void* Wq, const float* Ws, const void* bgu,
+                                   const int32_t* cnt, const int32_t* off, const int32_t* rows, int64_t T, int H,
+                                   int E, int k, int I, void* h, hipStream_t stream);
+hipError_t launch_gemv_fp8_down(const void* hq, const float* sh, const void* Wq, const float* Ws, const void* bd,
+                                const int32_t* cnt, const int32_t* off, int64_t T, int H, int E, int k, int I,
+                                float* o, hipStream_t stream);
 
 // slots with pos < 0 are left out; out_f32: y is float32 (partial sums), else bf16
 hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, int64_t T, int H, int k,

@@ -530,20 +530,22 @@ int moe_quantize_rows_fp8(const void* a, int64_t R, int32_t K, void* codes, floa
 static int run_gate_up_fp8(const char* fn, const void* xq, const float* sx, const void* Wq, const float* Ws,
                            const void* bgu, const int32_t* cnt, const int32_t* off, const int32_t* rows, int64_t T,
                            int32_t H, int32_t E, int32_t k, int32_t I, void* h, int32_t path, hipStream_t s) {
-  path = path == MOE_PATH_AUTO ? MOE_PATH_GEMM : path;
+  path = choose_path(path, T, E, k);
   if (path == MOE_PATH_GEMM)
     return hip_status(fn, moe::launch_gemm_fp8_gate_up(xq, sx, Wq, Ws, bgu, cnt, off, rows, T, H, E, k, I, h, s));
-  if (path == MOE_PATH_GEMV) return hip_status(fn, hipErrorNotSupported);
+  if (path == MOE_PATH_GEMV)
+    return hip_status(fn, moe::launch_gemv_fp8_gate_up(xq, sx, Wq, Ws, bgu, cnt, off, rows, T, H, E, k, I, h, s));
   return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
 }
 
 static int run_down_fp8(const char* fn, const void* hq, const float* sh, const void* Wq, const float* Ws,
                         const void* bd, const int32_t* cnt, const int32_t* off, int64_t T, int32_t H, int32_t E,
                         int32_t k, int32_t I, float* o, int32_t path, hipStream_t s) {
-  path = path == MOE_PATH_AUTO ? MOE_PATH_GEMM : path;
+  path = choose_path(path, T, E, k);
   if (path == MOE_PATH_GEMM)
     return hip_status(fn, moe::launch_gemm_fp8_down(hq, sh, Wq, Ws, bd, cnt, off, T, H, E, k, I, o, s));
-  if (path == MOE_PATH_GEMV) return hip_status(fn, hipErrorNotSupported);
+  if (path == MOE_PATH_GEMV)
+    return hip_status(fn, moe::launch_gemv_fp8_down(hq, sh, Wq, Ws, bd, cnt, off, T, H, E, k, I, o, s));
   return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
 }
 

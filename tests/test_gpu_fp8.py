@@ -21,7 +21,7 @@ from checks import assert_nan_rows, assert_routing, assert_y_close, bf16_bits, d
 
 pytestmark = pytest.mark.gpu
 
-PATHS = ["gemm"]
+PATHS = ["gemv", "gemm"]
 
 
 def _need_gpu():
