@@ -14,27 +14,29 @@
 // token's x row for gate_up, a (token, slot) row of h for down).  h is
 // rounded to bf16 by the gate_up epilogue and quantised by the row kernel.
 //
-// Tiled GEMM: the bf16 kernel's 128 x 512 tiles, (expert, m-tile) lookup,
-// XCD-aware order, three-buffer token LDS ring and barrier placement, with
-// v_mfma_f32_32x32x64_f8f6f4 (full rate at one wave per SIMD) on K steps of
-// 64 codes.  Each wave owns 128 x 128 = 4 x 4 blocks of 32 x 32.
-//   K slots: operand byte q of lane group g (g = lane/32) is K = 32*(q/16) +
-//   16g + q%16 of the step, for both operands, so every 16-byte load of
-//   either operand is contiguous in memory.
-//   B (codes [E][N][K], K contiguous): lane (c = lane%32, g) of wave w loads,
-//   for block j = 0..3, column n0 + 128w + 4c + j: two 16-byte loads, two
-//   steps ahead in a ring of two register sets, copied out at the step start
-//   so the set can be reloaded at once.
+// Tiled GEMM: the bf16 kernel's (expert, m-tile) lookup, XCD-aware order,
+// three-buffer token LDS ring and barrier placement, with
+// v_mfma_f32_16x16x128_f8f6f4 on K steps of 128 codes.  A workgroup covers
+// 128 rows x 256 columns; each of its four waves 128 x 64 = 8 x 4 blocks of
+// 16 x 16 (128 accumulators per lane).
+//   K slots: operand byte q of lane group g (g = lane/16) is K = 64*(q/16) +
+//   16g + q%16 of the step, for both operands, so the four lane groups' 16-byte
+//   loads of a column or token row are one contiguous 64-byte run.
+//   B (codes [E][N][K], K contiguous): lane (c = lane%16, g) of wave w loads,
+//   for block j = 0..3, column n0 + 64w + 4c + j: two 16-byte loads a step,
+//   issued back to back, which between them read the column's whole 128-byte
+//   line (reading the line across two steps instead costs the L2 twice the
+//   requests).  Two steps ahead, in a ring of three register sets.
 //   A (codes of token rows): gathered through rows[] (gate_up) or contiguous
-//   (down), two 16-byte pieces per thread four steps ahead, stored into the
-//   fragment-major LDS ring two steps ahead (so each load has two steps to
-//   arrive): fragment mi (rows 32mi..32mi+31) holds, in lane order, the 32
+//   (down); each thread copies four 16-byte pieces a step, eight threads per
+//   128-byte row, four steps ahead, into the fragment-major LDS ring two steps
+//   ahead: fragment mi (rows 16mi..16mi+15) holds, in lane order, the 32
 //   bytes lane l of the MFMA needs.
-// Epilogue: in the 32 x 32 accumulator layout lane l, element v holds row
-// 8*(v/4) + 4*(l/32) + v%4 of MFMA column l%32, i.e. weight column
-// n0 + 128w + 4c + j of block j: a lane holds two whole (gate, up) pairs.
-// Product * s_row * s_expert + bias, then GLU and one 4-byte bf16 h store
-// (gate_up) or one 16-byte float32 store (down).
+// Epilogue: in the 16 x 16 accumulator layout lane l, element v holds row
+// 4*(l/16) + v of MFMA column l%16, i.e. weight column n0 + 64w + 4c + j of
+// block j: a lane holds two whole (gate, up) pairs.  Product * s_row *
+// s_expert + bias, then GLU and one 4-byte bf16 h store (gate_up) or one
+// 16-byte float32 store (down).
 #include "device_common.h"
 #include "launch.h"
 
@@ -45,7 +47,6 @@ namespace moe {
 namespace {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kE4m3Max = 448.0f;
 
@@ -199,15 +200,15 @@ __global__ void fp8_scale_finalize_kernel(uint32_t* __restrict__ amax_to_scale, 
 constexpr int kFgThreads = 256;
 constexpr int kFgWaves = kFgThreads / kWave;
 constexpr int kFgBM = 128;
-constexpr int kFgWN = 128;
-constexpr int kFgBN = kFgWaves * kFgWN;   // 512
-constexpr int kFgBK = 64;                 // codes per K step
+constexpr int kFgWN = 64;
+constexpr int kFgBN = kFgWaves * kFgWN;   // 256
+constexpr int kFgBK = 128;                // codes per K step
 constexpr int kFgLdsBufs = 3;
 constexpr int kXcds = 8;
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
 struct FgSmem {
-  u32x4_t a[kFgLdsBufs][kFgBM / 32][kWave][2];   // 3 x 4 fragments x 2 KB
+  u32x4_t a[kFgLdsBufs][kFgBM / 16][kWave][2];   // 3 x 8 fragments x 2 KB
   float srow[kFgBM];
 };
 
@@ -227,13 +228,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4_t buf_ld16(rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
-__device__ __forceinline__ f32x16_t mfma_fp8(const u32x4_t (&a)[2], const u32x4_t (&b)[2], f32x16_t c) {
+__device__ __forceinline__ f32x4_t mfma_fp8_16(const u32x4_t (&a)[2], const u32x4_t (&b)[2], f32x4_t c) {
   const i32x8_t av = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
                       (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
   const i32x8_t bv = {(int)b[0].x, (int)b[0].y, (int)b[0].z, (int)b[0].w,
                       (int)b[1].x, (int)b[1].y, (int)b[1].z, (int)b[1].w};
   // format 0 (E4M3) for both operands, no block scales
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
 }
 
 template <bool GATE_UP>
@@ -289,85 +290,84 @@ __global__ __launch_bounds__(kFgThreads, 1) void gemm_fp8_kernel(
   const int row0 = off[e];
   const int n0 = nt * kFgBN;
 
-  // ---- A: thread t copies pieces p = t and t + 256 of the step: row p/4
-  // (rows past M read row M-1), 16 codes at K offset 16 (p%4); piece c4
-  // belongs to lane group c4%2, operand half c4/2 of fragment row/32 ----
+  // ---- A: thread t copies pieces p = t + 256 s (s = 0..3) of the step: row
+  // p/8 (rows past M read row M-1), 16 codes at K offset 16 (p%8); piece c8
+  // belongs to lane group c8%4, operand half c8/4 of fragment row/16 ----
   const rsrc_t a_rs = make_rsrc(A, (uint32_t)((size_t)a_rows * K));
-  const int a_c4 = tid & 3;
-  uint32_t a_off[2];
-  int a_frag[2], a_lane[2];
+  const int a_c8 = tid & 7;
+  uint32_t a_off[4];
+  int a_dst[4];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int row = (tid >> 2) + 64 * s;
+  for (int s = 0; s < 4; ++s) {
+    const int row = (tid >> 3) + 32 * s;
     const int m = min(m0 + row, M - 1);
     const uint32_t r = GATE_UP ? (uint32_t)(rows[row0 + m] / kslots) : (uint32_t)(row0 + m);
-    a_off[s] = r * (uint32_t)K + 16u * a_c4;
-    a_frag[s] = row >> 5;
-    a_lane[s] = (row & 31) + 32 * (a_c4 & 1);
+    a_off[s] = r * (uint32_t)K + 16u * a_c8;
+    a_dst[s] = ((row >> 4) * kWave + (row & 15) + 16 * (a_c8 & 3)) * 2 + (a_c8 >> 2);
   }
   if (tid < kFgBM) {
     const int m = min(m0 + tid, M - 1);
     sm.srow[tid] = GATE_UP ? a_scale[rows[row0 + m] / kslots] : a_scale[row0 + m];
   }
-  // ---- B: lane (c, g) of wave w, block j: column n0 + 128w + 4c + j ----
-  const int g = lane >> 5;
-  const int c = lane & 31;
+  // ---- B: lane (c, g) of wave w, block j: column n0 + 64w + 4c + j ----
+  const int g = lane >> 4;
+  const int c = lane & 15;
   const int cw = n0 + wave * kFgWN + 4 * c;
   const rsrc_t w_rs = make_rsrc(Wq + (size_t)e * N * K, (uint32_t)N * (uint32_t)K);
   uint32_t b_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) b_off[j] = (uint32_t)min(cw + j, N - 1) * (uint32_t)K + 16u * g;
 
-  auto gload_a = [&](int kt, u32x4_t (&ra)[2]) {
+  auto gload_a = [&](int kt, u32x4_t (&ra)[4]) {
     const uint32_t kb = (uint32_t)kt * kFgBK;
-    const bool ok = (int)kb + 16 * a_c4 < K;
+    const bool ok = (int)kb + 16 * a_c8 < K;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) ra[s] = buf_ld16(a_rs, ok ? a_off[s] + kb : kOutOfRange);
+    for (int s = 0; s < 4; ++s) ra[s] = buf_ld16(a_rs, ok ? a_off[s] + kb : kOutOfRange);
   };
   auto gload_b = [&](int kt, u32x4_t (&rb)[4][2]) {
     const uint32_t kb = (uint32_t)kt * kFgBK;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const bool ok = (int)kb + 32 * h + 16 * g < K;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) rb[j][h] = buf_ld16(w_rs, ok ? b_off[j] + kb + 32u * h : kOutOfRange);
-    }
+      for (int h = 0; h < 2; ++h) {
+        const bool ok = (int)kb + 64 * h + 16 * g < K;
+        rb[j][h] = buf_ld16(w_rs, ok ? b_off[j] + kb + 64u * h : kOutOfRange);
+      }
   };
-  auto lstore = [&](int kt, const u32x4_t (&ra)[2]) {
-    const int buf = kt % kFgLdsBufs;
+  u32x4_t* const lds_a = &sm.a[0][0][0][0];
+  auto lstore = [&](int kt, const u32x4_t (&ra)[4]) {
+    u32x4_t* const base = lds_a + (kt % kFgLdsBufs) * (kFgBM / 16) * kWave * 2;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) sm.a[buf][a_frag[s]][a_lane[s]][a_c4 >> 1] = ra[s];
+    for (int s = 0; s < 4; ++s) base[a_dst[s]] = ra[s];
   };
   auto lread = [&](int buf, int mi, u32x4_t (&f)[2]) {
     f[0] = sm.a[buf][mi][lane][0];
     f[1] = sm.a[buf][mi][lane][1];
   };
 
-  f32x16_t acc[4][4];
+  f32x4_t acc[8][4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][j][v] = 0.0f;
+    for (int j = 0; j < 4; ++j) acc[mi][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Registers (the loop is unrolled three times and no ring needs a register
   // copy): B of steps kt, kt+1, kt+2 (Rb[kt%3] is used by step kt and then
-  // reloaded, at step kt+1, with step kt+3), A of steps kt+2, kt+3 and kt+4
+  // reloaded, at step kt+1, with step kt+3); A of steps kt+2, kt+3 and kt+4
   // (Ra[j%3] holds A(j) from its load, four steps ahead, to its LDS store,
-  // two steps ahead), the A fragments F of step kt (each reloaded with step
+  // two steps ahead); the A fragments F of step kt (each reloaded with step
   // kt+1 after its last MFMA).
   u32x4_t Rb[3][4][2];
-  u32x4_t Ra[3][2];
-  u32x4_t F[4][2];
+  u32x4_t Ra[3][4];
+  u32x4_t F[8][2];
 
   // One K step kt (r = kt % 3): issue the loads of A(kt+4), then B(kt+2)
-  // (loads retire in order: the next step's store of A waits for A alone);
-  // multiply B(kt) with F, reading the fragments of kt+1 as those of kt
-  // retire; store A(kt+2); one barrier after the third of the four MFMA
-  // groups.  The LDS ring: buffer (kt+1)%3 is read during step kt, buffer
-  // (kt+2)%3 written before its barrier (its previous reads, of step kt-2,
-  // all precede the barrier of step kt-1).
+  // (loads retire in order: a later store of A waits for A alone); multiply
+  // B(kt) with F, reading the fragments of kt+1 as those of kt retire; store
+  // A(kt+2); one barrier after the fifth of the eight MFMA groups.  The LDS
+  // ring: buffer (kt+1)%3 is read during step kt, buffer (kt+2)%3 written
+  // before its barrier (its previous reads, of step kt-2, all precede the
+  // barrier of step kt-1).
   auto step = [&](int kt, auto rc) {
     constexpr int r = decltype(rc)::value;
     const u32x4_t (&bt)[4][2] = Rb[r];
@@ -377,36 +377,35 @@ __global__ __launch_bounds__(kFgThreads, 1) void gemm_fp8_kernel(
     const int nbuf = (kt + 1) % kFgLdsBufs;
     auto group = [&](int mi) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[mi][j] = mfma_fp8(F[mi], bt[j], acc[mi][j]);
+      for (int j = 0; j < 4; ++j) acc[mi][j] = mfma_fp8_16(F[mi], bt[j], acc[mi][j]);
     };
-    group(0);
-    lread(nbuf, 0, F[0]);
-    group(1);
-    lread(nbuf, 1, F[1]);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      group(mi);
+      lread(nbuf, mi, F[mi]);
+    }
     lstore(kt + 2, Ra[(r + 2) % 3]);
-    group(2);
+    group(4);
+    // the twelve global loads over the first twenty MFMAs
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 global load
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // 2 LDS reads
+    for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 global load
+      }
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // 2 LDS reads
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);     // 2 LDS writes
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);       // 4 LDS writes
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __syncthreads();
-    lread(nbuf, 2, F[2]);
-    group(3);
-    lread(nbuf, 3, F[3]);
+    lread(nbuf, 4, F[4]);
+#pragma unroll
+    for (int mi = 5; mi < 8; ++mi) {
+      group(mi);
+      lread(nbuf, mi, F[mi]);
+    }
   };
 
   // Prologue: the loads in the order the steps issue them (A(j+2), then
@@ -422,7 +421,7 @@ __global__ __launch_bounds__(kFgThreads, 1) void gemm_fp8_kernel(
   lstore(1, Ra[1]);
   __syncthreads();
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) lread(0, mi, F[mi]);
+  for (int mi = 0; mi < 8; ++mi) lread(0, mi, F[mi]);
 
   // The step count is rounded up to the unroll period: an extra step reads
   // only zeros (K past the end on both operands) and adds exactly 0.
@@ -447,10 +446,10 @@ __global__ __launch_bounds__(kFgThreads, 1) void gemm_fp8_kernel(
     bb[3] = bf16hi(b1);
   }
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rt = 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);   // row within the tile
+    for (int v = 0; v < 4; ++v) {
+      const int rt = 16 * mi + 4 * g + v;   // row within the tile
       const int m = m0 + rt;
       if (m < M) {
         const float sc = sm.srow[rt] * ws;
@@ -513,14 +512,6 @@ template <int MG>
 struct F8A {
   u32x4_t a[MG][2];
 };
-
-__device__ __forceinline__ f32x4_t mfma_fp8_16(const u32x4_t (&a)[2], const u32x4_t (&b)[2], f32x4_t c) {
-  const i32x8_t av = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
-                      (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
-  const i32x8_t bv = {(int)b[0].x, (int)b[0].y, (int)b[0].z, (int)b[0].w,
-                      (int)b[1].x, (int)b[1].y, (int)b[1].z, (int)b[1].w};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
-}
 
 template <bool GATE_UP, int MG>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 2 : 1))) void gemv_fp8_kernel(
