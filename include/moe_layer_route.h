@@ -245,6 +245,28 @@ MOE_API int moe_combine(const float* o, const int32_t* pos, const float* topk_w,
                 int64_t T, int32_t H, int32_t k, void* y, void* stream);
 
 /*
+ * moe_forward_padded -- moe_forward for a statically sized batch whose tail
+ * is padding, with the per-expert loads exported.  The verify-graph page
+ * (static buffers, pad tails zeroed for determinism) and the Phase 19 page's
+ * per-layer expert-load recorder are the callers this serves.
+ *   n_valid            device int32 (nullable: every row valid), read on the
+ *                      device when the call runs, clamped to [0, T): rows
+ *                      t >= n_valid are padding.  A padding row is routed to no
+ *                      expert (topk_ids -1, topk_w 0), costs no expert work,
+ *                      and its y row is 0.  Grids are sized from T alone, so a
+ *                      captured graph replays with any n_valid.
+ *   expert_counts_out  device int32 [E] (nullable): cnt[e], the number of
+ *                      (valid token, slot) pairs routed to expert e.
+ * Every other argument is as in moe_forward_ex (workspace: moe_workspace_bytes).
+ */
+MOE_API int moe_forward_padded(const void* x, const void* Wr, const void* br,
+                               const void* Wgu, const void* bgu, const void* Wd, const void* bd,
+                               int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                               const int32_t* n_valid, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                               int32_t* expert_counts_out, void* workspace, size_t workspace_bytes,
+                               int32_t path, void* stream);
+
+/*
  * MXFP4 expert weights (W4A16) -- xserv "Phase 19: gpt-oss-20b MoE support",
  * section 5: the expert weights are 4-bit E2M1 values with one UE8M0
  * (power-of-two) scale per 32 values; activations, biases, the router and

@@ -27,7 +27,7 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace
            "moe_forward", "moe_forward_ex", "moe_forward_ep", "moe_permute", "moe_gate_up", "moe_down",
            "moe_combine", "moe_quantize_mxfp4", "moe_forward_mxfp4", "moe_forward_mxfp4_ex", "moe_gate_up_mxfp4",
            "moe_down_mxfp4", "moe_quantize_fp8", "moe_quantize_rows_fp8", "moe_workspace_bytes_fp8",
-           "moe_forward_fp8", "moe_forward_fp8_ex", "moe_gate_up_fp8", "moe_down_fp8")
+           "moe_forward_fp8", "moe_forward_fp8_ex", "moe_gate_up_fp8", "moe_down_fp8", "moe_forward_padded")
 
 
 class MoEError(RuntimeError):
@@ -59,6 +59,7 @@ _SIGS = {
     "moe_gate_up_mxfp4": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
     "moe_down_mxfp4": (ctypes.c_int, [_vp] * 6 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
     "moe_quantize_fp8": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "moe_forward_padded": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 5 + [_vp, _sz, _i32, _vp]),
     "moe_quantize_rows_fp8": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp]),
     "moe_workspace_bytes_fp8": (_sz, [_i64, _i32, _i32, _i32, _i32]),
     "moe_forward_fp8": (ctypes.c_int, [_vp] * 9 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _vp]),
@@ -438,3 +439,30 @@ def moe_down_fp8(hq, sh, Wd_q, Wd_s, bd, cnt, off, T: int, k: int, o=None, path=
     _check(library().moe_down_fp8(_ptr(hq), _ptr(sh), _ptr(Wd_q), _ptr(Wd_s), _ptr(bd), _ptr(cnt), _ptr(off), T, H,
                                   E, k, I, _ptr(o), path_code(path), _stream(stream)), "moe_down_fp8")
     return o
+
+
+def moe_forward_padded(x, Wr, br, Wgu, bgu, Wd, bd, k: int = 4, n_valid=None, y=None, workspace=None,
+                       topk_ids=None, topk_w=None, expert_counts=None, path="auto", stream=None):
+    """moe_forward over a batch whose rows from n_valid (a device int32
+    tensor of one element, read when the call runs) are padding; returns y.
+    expert_counts (device int32 [E]), if given, receives the per-expert loads."""
+    _dev(x, Wr, br, Wgu, bgu, Wd, bd)
+    _b16(x, Wr, br, Wgu, bgu, Wd, bd)
+    T, H = x.shape
+    E = Wr.shape[0]
+    I = Wd.shape[1]
+    if n_valid is not None and (n_valid.dtype != torch.int32 or n_valid.numel() != 1):
+        raise MoEError("n_valid must be a one-element int32 tensor")
+    if expert_counts is not None and (expert_counts.dtype != torch.int32 or expert_counts.numel() != E):
+        raise MoEError("expert_counts must be an int32 tensor of E elements")
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(T, H, E, k, I, x.device)
+    _dev(y, workspace, topk_ids, topk_w, n_valid, expert_counts)
+    st = library().moe_forward_padded(_ptr(x), _ptr(Wr), _ptr(br), _ptr(Wgu), _ptr(bgu), _ptr(Wd), _ptr(bd), T, H,
+                                      E, k, I, _ptr(n_valid), _ptr(y), _ptr(topk_ids), _ptr(topk_w),
+                                      _ptr(expert_counts), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), path_code(path), _stream(stream))
+    _check(st, "moe_forward_padded")
+    return y

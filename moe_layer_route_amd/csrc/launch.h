@@ -19,6 +19,9 @@ hipError_t launch_route(const void* x, const void* Wr, const void* br, int64_t T
 // [e_begin, e_begin + E) are skipped (pos = -1)
 hipError_t launch_permute(const int32_t* ids, int64_t T, int E, int k, int32_t* cnt, int32_t* off,
                           int32_t* rows, int32_t* pos, hipStream_t stream, int e_begin = 0);
+// slots of tokens t >= *n_valid (device int32) -> id -1, weight 0
+hipError_t launch_mask_padding(int32_t* ids, float* w, int64_t T, int k, const int32_t* n_valid,
+                               hipStream_t stream);
 
 // Weight-streaming expert kernels (small token counts per expert).
 hipError_t launch_gemv_gate_up(const void* x, const void* Wgu, const void* bgu, const int32_t* cnt,

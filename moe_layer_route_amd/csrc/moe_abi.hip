@@ -262,6 +262,59 @@ int moe_forward_ep(const void* x, const void* Wr, const void* br, const void* Wg
   return ok();
 }
 
+int moe_forward_padded(const void* x, const void* Wr, const void* br, const void* Wgu, const void* bgu,
+                       const void* Wd, const void* bd, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                       const int32_t* n_valid, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                       int32_t* expert_counts_out, void* workspace, size_t workspace_bytes, int32_t path,
+                       void* stream) {
+  const char* fn = "moe_forward_padded";
+  if (int st = check_dims(fn, T, H, E, k, I)) return st;
+  CHECK_PTR(x, 16);
+  CHECK_PTR(Wr, 16);
+  CHECK_PTR(br, 2);
+  CHECK_PTR(Wgu, 16);
+  CHECK_PTR(bgu, 4);
+  CHECK_PTR(Wd, 16);
+  CHECK_PTR(bd, 4);
+  CHECK_PTR(y, 16);
+  if (n_valid && !aligned(n_valid, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: n_valid is not 4-byte aligned", fn);
+  if (topk_ids_out && !aligned(topk_ids_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_ids_out is not 4-byte aligned", fn);
+  if (topk_w_out && !aligned(topk_w_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_w_out is not 4-byte aligned", fn);
+  if (expert_counts_out && !aligned(expert_counts_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s: expert_counts_out is not 4-byte aligned", fn);
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+  if (T == 0) return ok();
+  const Layout L = layout(T, H, E, k, I);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, L.total);
+  if (!aligned(workspace, 256))
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* cnt = expert_counts_out ? expert_counts_out : reinterpret_cast<int32_t*>(ws + L.cnt);
+  int32_t* off = reinterpret_cast<int32_t*>(ws + L.off);
+  int32_t* rows = reinterpret_cast<int32_t*>(ws + L.rows);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+  void* h = ws + L.h;
+  float* o = reinterpret_cast<float*>(ws + L.o);
+  hipStream_t s = (hipStream_t)stream;
+
+  if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, ids, w, MOE_ROUTE_AUTO, s))) return st;
+  if (n_valid)
+    if (int st = hip_status(fn, moe::launch_mask_padding(ids, w, T, k, n_valid, s))) return st;
+  if (int st = hip_status(fn, moe::launch_permute(ids, T, E, k, cnt, off, rows, pos, s))) return st;
+  if (int st = run_gate_up(fn, x, Wgu, bgu, cnt, off, rows, T, H, E, k, I, h, path, s)) return st;
+  if (int st = run_down(fn, h, Wd, bd, cnt, off, T, H, E, k, I, o, path, s)) return st;
+  if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s))) return st;
+  return ok();
+}
+
 int moe_forward(const void* x, const void* Wr, const void* br, const void* Wgu, const void* bgu,
                 const void* Wd, const void* bd, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
                 void* y, int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,

@@ -198,6 +198,20 @@ __global__ __launch_bounds__(256) void permute_inverse_kernel(const int32_t* __r
   if (i < off[E]) pos[rows[i]] = i;
 }
 
+// Padding rows of a statically sized batch: slots of tokens t >= *n_valid
+// (read on the device, clamped to [0, T]) get id -1 and weight 0, so the
+// permutation skips them (pos = -1) and no expert ever sees them.
+__global__ void mask_padding_kernel(int32_t* __restrict__ ids, float* __restrict__ w, int64_t T, int k,
+                                    const int32_t* __restrict__ n_valid) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * k) return;
+  const int64_t nv = min(max((int64_t)*n_valid, (int64_t)0), T);
+  if (i / k >= nv) {
+    ids[i] = -1;
+    w[i] = 0.0f;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_permute(const int32_t* ids, int64_t T, int E, int k, int32_t* cnt, int32_t* off,
@@ -218,6 +232,15 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int E, int k, int32_t* 
                      (const int32_t*)pos, nchunks, cnt, off, rows, (int32_t*)nullptr);
   hipLaunchKernelGGL(permute_inverse_kernel, dim3((S + 255) / 256), dim3(256), 0, stream, ids, S, e_begin,
                      (const int32_t*)rows, (const int32_t*)off, E, pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_padding(int32_t* ids, float* w, int64_t T, int k, const int32_t* n_valid,
+                               hipStream_t stream) {
+  const int64_t n = T * k;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mask_padding_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, ids, w, T, k,
+                     n_valid);
   return hipGetLastError();
 }
 

@@ -193,6 +193,32 @@ def _forward(x, Wr, br, weights, I2, Hout, k, tokens=None, keep=False, experts=N
 
 
 # --------------------------------------------------------------------------
+# Padded batches and expert loads (the verify-graph page: statically sized
+# buffers whose tail rows are padding; the Phase 19 page: a per-layer
+# recorder of how many routed slots each expert receives)
+# --------------------------------------------------------------------------
+def expert_loads(ids: np.ndarray, E: int) -> np.ndarray:
+    """Number of (token, slot) pairs routed to each expert; ids < 0 are not routed."""
+    flat = ids.reshape(-1)
+    return np.bincount(flat[flat >= 0], minlength=E)
+
+
+def moe_forward_padded(x, Wr, br, Wgu, bgu, Wd, bd, k: int, n_valid: int):
+    """Rows t >= n_valid (clamped to [0, T]) are padding: routed nowhere (id
+    -1, weight 0), y = 0; the other rows are moe_forward of those rows alone.
+    Also returns the expert loads of the valid rows."""
+    T, E = x.shape[0], Wr.shape[0]
+    nv = min(max(int(n_valid), 0), T)
+    y = np.zeros((T, Wd.shape[2]))
+    ids = np.full((T, k), -1, dtype=np.int32)
+    w = np.zeros((T, k))
+    if nv:
+        r = moe_forward(x[:nv], Wr, br, Wgu, bgu, Wd, bd, k=k)
+        y[:nv], ids[:nv], w[:nv] = r["y"], r["ids"], r["w"]
+    return {"y": y, "ids": ids, "w": w, "loads": expert_loads(ids, E)}
+
+
+# --------------------------------------------------------------------------
 # MXFP4 expert weights (section 5 of the Phase 19 page, "MXFP4 W4A16": the
 # weights are 4-bit E2M1 values with one UE8M0 power-of-two scale per 32
 # values; activations stay bf16).  Readings (listed in DESIGN.md):

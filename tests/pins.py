@@ -475,6 +475,34 @@ def pin_mxfp4_forward(orc):
 
 
 # ---------------------------------------------------------------------------
+# Padded batches and expert loads
+# ---------------------------------------------------------------------------
+def pin_padded_batches(orc):
+    """Loads equal a scalar count over the valid slots; padding rows are zero
+    and routed nowhere; valid rows do not depend on what the padding holds;
+    n_valid is clamped to [0, T]."""
+    T, E, H, I, k = 9, 6, 40, 24, 2
+    x, Wr, br, Wgu, bgu, Wd, bd = _tiny_inputs(91, T, E, H, I, 1.5)
+    for nv in (0, 1, 5, T, T + 3, -2):
+        got = orc.moe_forward_padded(x, Wr, br, Wgu, bgu, Wd, bd, k=k, n_valid=nv)
+        n = min(max(nv, 0), T)
+        assert (got["y"][n:] == 0).all() and (got["ids"][n:] == -1).all() and (got["w"][n:] == 0).all(), nv
+        count = [0] * E
+        for t in range(n):
+            for j in range(k):
+                count[int(got["ids"][t, j])] += 1
+        assert list(got["loads"]) == count, (nv, list(got["loads"]), count)
+        assert sum(count) == n * k
+        x2 = x.copy()
+        x2[n:] = _bf(np.random.default_rng(nv + 7).normal(0, 30, (T - n, H)))
+        other = orc.moe_forward_padded(x2, Wr, br, Wgu, bgu, Wd, bd, k=k, n_valid=nv)
+        assert (other["y"] == got["y"]).all() and (other["loads"] == got["loads"]).all(), nv
+        if n:
+            alone = orc.moe_forward(x[:n], Wr, br, Wgu, bgu, Wd, bd, k=k)
+            assert np.abs(alone["y"] - got["y"][:n]).max() <= 1e-12 * max(1.0, np.abs(alone["y"]).max())
+
+
+# ---------------------------------------------------------------------------
 # FP8 W8A8 (section 5 of the Phase 19 page: 8-bit weights with one scale per
 # expert; the OCP E4M3 format: sign, 4 exponent bits with bias 7, 3 mantissa
 # bits, no infinities, S.1111.111 NaN, largest finite 1.75 * 2^8 = 448)
@@ -669,4 +697,5 @@ ALL_PINS = [pin_glu, pin_topk, pin_router, pin_permutation, pin_forward_brutefor
             pin_identical_experts, pin_structured_experts, pin_skip_semantics, pin_expert_ranges,
             pin_identity_glu_table, pin_e2m1_table, pin_ue8m0, pin_mxfp4_layout, pin_mxfp4_quantize_rne,
             pin_mxfp4_nearest, pin_mxfp4_forward, pin_e4m3_table, pin_e4m3_encode, pin_fp8_scales,
-            pin_fp8_weight_layout, pin_fp8_gate_up_exact, pin_fp8_down_exact, pin_fp8_forward_structure]
+            pin_fp8_weight_layout, pin_fp8_gate_up_exact, pin_fp8_down_exact, pin_fp8_forward_structure,
+            pin_padded_batches]

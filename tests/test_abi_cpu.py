@@ -210,3 +210,17 @@ def test_fp8_calls_validate(lib):
     assert lib.moe_quantize_rows_fp8(v, 4, 24, v, v, None) == INVALID and b"K=24" in lib.moe_last_error()
     assert lib.moe_quantize_rows_fp8(v, 4, 64, v, ctypes.c_void_p(FAKE + 2), None) == INVALID
     assert lib.moe_workspace_bytes_fp8(4, 64, 0, 2, 64) == 0
+
+
+def test_padded_calls_validate(lib):
+    v = ctypes.c_void_p(FAKE)
+    p = [ctypes.c_void_p(FAKE)] * 8
+
+    def call(n_valid=None, counts=None, path=0, T=4, ws=1 << 30):
+        return lib.moe_forward_padded(*p[:7], T, 64, 8, 2, 64, n_valid, p[7], None, None, counts, v, ws, path, None)
+
+    assert call(n_valid=ctypes.c_void_p(FAKE + 2)) == INVALID and b"n_valid" in lib.moe_last_error()
+    assert call(counts=ctypes.c_void_p(FAKE + 1)) == INVALID and b"expert_counts_out" in lib.moe_last_error()
+    assert call(path=9) == INVALID and b"unknown path" in lib.moe_last_error()
+    assert call(ws=16) == WORKSPACE
+    assert call(T=0, n_valid=v, counts=v) == OK

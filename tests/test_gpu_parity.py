@@ -371,6 +371,77 @@ def test_graph_capture_replay():
 
 
 # ---------------------------------------------------------------------------
+# padded batches (device-side valid-row count) and expert loads
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("nv", [0, 1, 37, 64, 80])
+def test_padded_forward(path, nv):
+    """Rows from n_valid on are padding: id -1, weight 0, y exactly 0, no
+    expert load; the valid rows and the loads match the oracle."""
+    _need_gpu()
+    T, E, H, I, k = 64, 16, 256, 160, 4
+    inp = _small_inputs(T, E, H, I, k, seed=13)
+    args = [dev(a) for a in inp.arrays()]
+    n_valid = torch.tensor([nv], dtype=torch.int32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts = torch.empty((E,), dtype=torch.int32, device="cuda")
+    y = binding.moe_forward_padded(*args, k=k, n_valid=n_valid, topk_ids=ids, topk_w=w, expert_counts=counts,
+                                   path=path)
+    ref = orc.moe_forward_padded(*inp.arrays(), k=k, n_valid=nv)
+    n = min(nv, T)
+    yb, idh, wh = bf16_bits(y), ids.cpu().numpy(), w.cpu().numpy()
+    assert (yb[n:] == 0).all() and (idh[n:] == -1).all() and (wh[n:] == 0).all()
+    assert (counts.cpu().numpy() == ref["loads"]).all(), (counts.cpu().numpy(), ref["loads"])
+    if n:
+        assert_routing(idh[:n], wh[:n], ref["ids"][:n], ref["w"][:n], None, k)
+        assert_y_close(host_f64(y)[:n], ref["y"][:n], f"y n_valid={nv}")
+
+
+def test_padded_graph_replay():
+    """One capture, replayed with a different n_valid each time: every replay
+    equals the eager call for that n_valid (y, ids and loads, bit for bit)."""
+    _need_gpu()
+    T, E, H, I, k = 64, 32, 2880, 2880, 4
+    inp = _small_inputs(T, E, H, I, k, seed=17)
+    args = [dev(a) for a in inp.arrays()]
+    ws = binding.alloc_workspace(T, H, E, k, I)
+    n_valid = torch.tensor([T], dtype=torch.int32, device="cuda")
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts = torch.empty((E,), dtype=torch.int32, device="cuda")
+
+    def call():
+        binding.moe_forward_padded(*args, k=k, n_valid=n_valid, y=y, workspace=ws, topk_ids=ids, topk_w=w,
+                                   expert_counts=counts)
+
+    eager = {}
+    for nv in (64, 10, 0, 37):
+        n_valid.fill_(nv)
+        call()
+        torch.cuda.synchronize()
+        eager[nv] = (bf16_bits(y).copy(), ids.cpu().numpy().copy(), counts.cpu().numpy().copy())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for nv in (37, 0, 64, 10, 37):
+        y.view(torch.int16).fill_(-1)
+        ws.fill_(0xAB)
+        n_valid.fill_(nv)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        yb, idh, ch = eager[nv]
+        assert (bf16_bits(y) == yb).all() and (ids.cpu().numpy() == idh).all() and (counts.cpu().numpy() == ch).all(), nv
+
+
+# ---------------------------------------------------------------------------
 # the five workloads at full size
 # ---------------------------------------------------------------------------
 _weights_cache = {}

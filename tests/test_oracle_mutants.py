@@ -12,7 +12,7 @@ _real = {n: getattr(orc, n) for n in ("clamped_glu", "router_logits", "select_to
                                       "moe_forward", "widen", "mxfp4_quantize", "mxfp4_dequantize",
                                       "moe_forward_mxfp4", "ue8m0_decode", "e2m1_decode", "e4m3_encode",
                                       "fp8_scale", "fp8_quantize_rows", "fp8_quantize_weights", "bf16_round",
-                                      "moe_forward_fp8", "fp8_down")}
+                                      "moe_forward_fp8", "fp8_down", "expert_loads", "moe_forward_padded")}
 
 
 def _glu(gate_sel=0, up_sel=1, alpha=1.702, glim=(-np.inf, 7.0), ulim=(-7.0, 7.0), plus=1.0,
@@ -280,7 +280,27 @@ def _fp8_down_no_weight_scale(hb, Wd_q_e, s_d_e, bd_e64):
     return _real["fp8_down"](hb, Wd_q_e, np.float32(1.0), bd_e64)
 
 
+def _loads_first_pick_only(ids, E):
+    first = ids[:, 0]
+    return np.bincount(first[first >= 0], minlength=E)
+
+
+def _padded_variant(route_padding=False, off_by_one=False):
+    def f(x, Wr, br, Wgu, bgu, Wd, bd, k, n_valid):
+        T = x.shape[0]
+        nv = min(max(int(n_valid), 0), T)
+        if route_padding:
+            nv = T
+        if off_by_one:
+            nv = max(nv - 1, 0)
+        return _real["moe_forward_padded"](x, Wr, br, Wgu, bgu, Wd, bd, k, nv)
+    return f
+
+
 MUTANTS = {
+    "loads_first_pick_only": ("expert_loads", _loads_first_pick_only),
+    "padded_rows_routed": ("moe_forward_padded", _padded_variant(route_padding=True)),
+    "padded_n_valid_off_by_one": ("moe_forward_padded", _padded_variant(off_by_one=True)),
     "e4m3_exponent_bias_8": ("E4M3_VALUES", _e4m3_table_bias8()),
     "e4m3_encode_ties_away": ("e4m3_encode", _encode_variant(ties="away")),
     "e4m3_encode_overflow_nan": ("e4m3_encode", _encode_variant(saturate=False)),
