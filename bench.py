@@ -211,6 +211,8 @@ def main(argv=None):
     ap.add_argument("--ep", type=int, default=1,
                     help="also time one expert-parallel rank's share of W ranks: experts [0, E/W), "
                          "all tokens routed (reported in ep_rank_share, not in value)")
+    ap.add_argument("--n-valid", type=int, default=None,
+                    help="also time moe_forward_padded with this many valid rows (the rest padding), bf16 weights")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy, the reference kernel "
                          "that scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -414,6 +416,32 @@ def main(argv=None):
     layer_flops = _alg_flops_layer(cfg)
     step_s = ms_per_step * 1e-3
 
+    padded = None
+    if args.n_valid is not None and not (mx or f8):
+        nv_t = torch.tensor([args.n_valid], dtype=torch.int32, device="cuda")
+        counts = torch.empty((E,), dtype=torch.int32, device="cuda")
+
+        def pad_step():
+            binding.moe_forward_padded(x, Wr, br, Wgu, bgu, Wd, bd, k=k, n_valid=nv_t, y=y, workspace=ws,
+                                       topk_ids=ids, topk_w=w, expert_counts=counts, path=args.path, stream=stream)
+
+        for _ in range(args.warmup):
+            pad_step()
+        torch.cuda.synchronize()
+        p0 = torch.cuda.Event(enable_timing=True)
+        p1 = torch.cuda.Event(enable_timing=True)
+        p0.record(stream)
+        for _ in range(args.steps):
+            pad_step()
+        p1.record(stream)
+        torch.cuda.synchronize()
+        pad_ms = p0.elapsed_time(p1) / args.steps
+        nv = min(max(args.n_valid, 0), T)
+        padded = {"n_valid": nv, "ms_per_step": pad_ms, "valid_tokens_per_s": nv / (pad_ms * 1e-3),
+                  "live_experts": int((counts > 0).sum().item()), "max_expert_load": int(counts.max().item())}
+        print(f"[bench] padded batch ({nv} of {T} rows valid): {pad_ms * 1e3:.1f} us/step", file=sys.stderr,
+              flush=True)
+
     ep_share = None
     if args.ep > 1:
         if E % args.ep:
@@ -469,6 +497,7 @@ def main(argv=None):
         "graph_ms_per_step": graph_ms,
         "achievable": _achievable(torch),
         "ep_rank_share": ep_share,
+        "padded": padded,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

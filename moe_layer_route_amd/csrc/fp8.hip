@@ -488,9 +488,11 @@ hipError_t launch_gemm(const void* A, const float* a_scale, const void* Wq, cons
 }
 
 // ---------------------------------------------------------------------------
-// Weight-streaming kernel (few rows per expert): one wave per workgroup, one
-// expert x 64 output columns over the whole of K (no K split, no LDS, no
-// barrier), v_mfma_f32_16x16x128_f8f6f4 on K steps of 128 codes.
+// Weight-streaming kernel (few rows per expert): a workgroup owns one expert
+// and 64 output columns; its four waves split K and stream their part of the
+// columns straight from HBM (no LDS staging), v_mfma_f32_16x16x128_f8f6f4 on
+// K steps of 128 codes.  The four partial sums are added in LDS in a fixed
+// order.
 //   K slots: operand byte q of lane group g (g = lane/16) is K = 64*(q/16) +
 //   16g + q%16 of the step, so lane (c = lane%16, g)'s two 16-byte pieces of
 //   a column, together with the other three groups', read the column's 128
@@ -501,8 +503,9 @@ hipError_t launch_gemm(const void* A, const float* a_scale, const void* Wq, cons
 //   register sets (32 bytes per lane and column a step: a deeper ring would
 //   leave one wave per SIMD), token rows (L2-resident) one step ahead.
 // ---------------------------------------------------------------------------
+constexpr int kF8Waves = 4;
 constexpr int kF8NJ = 4;                 // columns per lane
-constexpr int kF8Cols = 16 * kF8NJ;      // 64 columns per wave
+constexpr int kF8Cols = 16 * kF8NJ;      // 64 columns per workgroup
 constexpr int kF8BK = 128;               // codes per K step
 
 struct F8W {
@@ -514,7 +517,8 @@ struct F8A {
 };
 
 template <bool GATE_UP, int MG>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 2 : 1))) void gemv_fp8_kernel(
+__global__ __launch_bounds__(kF8Waves * kWave) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 2 : 1)))
+void gemv_fp8_kernel(
     const uint8_t* __restrict__ A,        // gate_up: x codes [T][K]; down: h codes [S][K] (permuted order)
     const float* __restrict__ a_scale,    // gate_up: [T]; down: [S]
     const uint8_t* __restrict__ Wq,       // [E][N][K]
@@ -523,11 +527,14 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(MG == 1 ?
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ off,
     const int32_t* __restrict__ rows,     // gate_up only: permuted slot ids
     int K, int N, int kslots, int a_rows, void* __restrict__ out) {
+  __shared__ float red[kF8Waves][kF8NJ][4][kWave];   // 16 KB: one 16-row chunk's partial sums per wave
+
   const int e = blockIdx.y;
   const int M = cnt[e];
-  if (M == 0) return;   // the whole (one-wave) workgroup: no load for an expert without rows
+  if (M == 0) return;   // block-uniform: no load, no barrier for an expert without rows
   const int row0 = off[e];
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = lane >> 4;
   const int c = lane & 15;
   // N % 4 == 0 and ncol % 4 == 0: a lane's four columns are all in range or all out
@@ -540,10 +547,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(MG == 1 ?
 #pragma unroll
   for (int j = 0; j < kF8NJ; ++j) w_off[j] = (uint32_t)min(ncol + j, N - 1) * (uint32_t)K + 16u * g;
   const int nk = (K + kF8BK - 1) / kF8BK;
+  const int kb_begin = (nk * wave) / kF8Waves;
+  const int kb_end = (nk * (wave + 1)) / kF8Waves;
   const float ws = w_scale[e];
 
   for (int r0 = 0; r0 < M; r0 += 16 * MG) {
-    const int nch = min(MG, (M - r0 + 15) / 16);   // uniform
+    const int nch = min(MG, (M - r0 + 15) / 16);   // block-uniform
     uint32_t a_off[MG];
 #pragma unroll
     for (int qq = 0; qq < MG; ++qq) {
@@ -557,12 +566,13 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(MG == 1 ?
 #pragma unroll
       for (int j = 0; j < kF8NJ; ++j) acc[qq][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // loads of step q; pieces past K read 0 (sent outside the descriptors)
+    // loads of step q; steps outside this wave's range and pieces past K
+    // read 0 (sent outside the descriptors, no memory touched)
     auto load_w = [&](int q, F8W& d) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t kb = (uint32_t)(q * kF8BK + 64 * h);
-        const bool in = (int)kb + 16 * g < K;
+        const bool in = q < kb_end && (int)kb + 16 * g < K;
 #pragma unroll
         for (int j = 0; j < kF8NJ; ++j) d.w[j][h] = buf_ld16(w_rs, in ? w_off[j] + kb : kOutOfRange);
       }
@@ -571,7 +581,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(MG == 1 ?
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t kb = (uint32_t)(q * kF8BK + 64 * h);
-        const bool in = (int)kb + 16 * g < K;
+        const bool in = q < kb_end && (int)kb + 16 * g < K;
 #pragma unroll
         for (int qq = 0; qq < MG; ++qq) d.a[qq][h] = buf_ld16(a_rs, in ? a_off[qq] + kb : kOutOfRange);
       }
@@ -589,11 +599,11 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(MG == 1 ?
 
     F8W w0, w1, w2;
     F8A<MG> a0, a1, a2;
-    load_w(0, w0);
-    load_w(1, w1);
-    load_a(0, a0);
-    int q = 0;
-    for (; q + 3 <= nk; q += 3) {
+    load_w(kb_begin, w0);
+    load_w(kb_begin + 1, w1);
+    load_a(kb_begin, a0);
+    int q = kb_begin;
+    for (; q + 3 <= kb_end; q += 3) {
       load_w(q + 2, w2);
       load_a(q + 1, a1);
       step(w0, a0);
@@ -605,46 +615,55 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(MG == 1 ?
       step(w2, a2);
     }
     // 0..2 steps left; w0, w1 hold steps q, q+1 and a0 holds step q
-    if (q < nk) {
+    if (q < kb_end) {
       load_a(q + 1, a1);
       step(w0, a0);
     }
-    if (q + 1 < nk) step(w1, a1);
+    if (q + 1 < kb_end) step(w1, a1);
 
-    // epilogue: 16x16 accumulator layout, lane (c, g) element v holds row
-    // 4g + v of MFMA column c = weight column ncol + j of call j
-    if (col_ok) {
-      float bb[kF8NJ];
-      {
-        const uint32_t* bp = reinterpret_cast<const uint32_t*>(bias + (size_t)e * N + ncol);
-        const uint32_t b01 = bp[0], b23 = bp[1];
-        bb[0] = bf16lo(b01);
-        bb[1] = bf16hi(b01);
-        bb[2] = bf16lo(b23);
-        bb[3] = bf16hi(b23);
-      }
+    // Sum the four K partials (fixed order: wave 0, 1, 2, 3); wave w then
+    // finishes accumulator element v = w (row 4g + w of each chunk) of all
+    // four columns.
+    float bb[kF8NJ];
+    {
+      const uint32_t* bp = reinterpret_cast<const uint32_t*>(bias + (size_t)e * N + min(ncol, N - kF8NJ));
+      const uint32_t b01 = bp[0], b23 = bp[1];
+      bb[0] = bf16lo(b01);
+      bb[1] = bf16hi(b01);
+      bb[2] = bf16lo(b23);
+      bb[3] = bf16hi(b23);
+    }
 #pragma unroll
-      for (int qq = 0; qq < MG; ++qq) {
-        if (qq < nch) {
+    for (int qq = 0; qq < MG; ++qq) {
+      if (qq < nch) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int m = r0 + 16 * qq + 4 * g + v;
-            if (m < M) {
-              const size_t orow = (size_t)(row0 + m);
-              const float sc = (GATE_UP ? a_scale[rows[row0 + m] / kslots] : a_scale[orow]) * ws;
-              if (GATE_UP) {
-                const float h0 = clamped_glu(acc[qq][0][v] * sc + bb[0], acc[qq][1][v] * sc + bb[1]);
-                const float h1 = clamped_glu(acc[qq][2][v] * sc + bb[2], acc[qq][3][v] * sc + bb[3]);
-                *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + orow * (N / 2) + ncol / 2) =
-                    pack_bf16x2(h0, h1);
-              } else {
-                *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + orow * N + ncol) =
-                    f32x4_t{acc[qq][0][v] * sc + bb[0], acc[qq][1][v] * sc + bb[1], acc[qq][2][v] * sc + bb[2],
-                            acc[qq][3][v] * sc + bb[3]};
-              }
-            }
+        for (int j = 0; j < kF8NJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[qq][j][v];
+        __syncthreads();
+        float sum[kF8NJ];
+#pragma unroll
+        for (int j = 0; j < kF8NJ; ++j) {
+          float t = 0.f;
+#pragma unroll
+          for (int w2 = 0; w2 < kF8Waves; ++w2) t += red[w2][j][wave][lane];
+          sum[j] = t;
+        }
+        const int m = r0 + 16 * qq + 4 * g + wave;
+        if (m < M && col_ok) {
+          const size_t orow = (size_t)(row0 + m);
+          const float sc = (GATE_UP ? a_scale[rows[row0 + m] / kslots] : a_scale[orow]) * ws;
+          if (GATE_UP) {
+            const float h0 = clamped_glu(sum[0] * sc + bb[0], sum[1] * sc + bb[1]);
+            const float h1 = clamped_glu(sum[2] * sc + bb[2], sum[3] * sc + bb[3]);
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + orow * (N / 2) + ncol / 2) =
+                pack_bf16x2(h0, h1);
+          } else {
+            *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + orow * N + ncol) =
+                f32x4_t{sum[0] * sc + bb[0], sum[1] * sc + bb[1], sum[2] * sc + bb[2], sum[3] * sc + bb[3]};
           }
         }
+        __syncthreads();
       }
     }
   }
@@ -661,7 +680,7 @@ hipError_t launch_gemv(const void* A, const float* a_scale, const void* Wq, cons
   // 32 rows per pass once the mean load per expert passes 10 rows
   const bool one = S <= 10 * (int64_t)E;
   auto kern = one ? gemv_fp8_kernel<GATE_UP, 1> : gemv_fp8_kernel<GATE_UP, 2>;
-  hipLaunchKernelGGL(kern, grid, dim3(kWave), 0, stream, (const uint8_t*)A, a_scale, (const uint8_t*)Wq, w_scale,
+  hipLaunchKernelGGL(kern, grid, dim3(kF8Waves * kWave), 0, stream, (const uint8_t*)A, a_scale, (const uint8_t*)Wq, w_scale,
                      (const bf16_t*)bias, cnt, off, rows, K, N, GATE_UP ? k : 1, (int)a_rows, out);
   return hipGetLastError();
 }
