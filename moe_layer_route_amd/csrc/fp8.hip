@@ -499,9 +499,14 @@ hipError_t launch_gemm(const void* A, const float* a_scale, const void* Wq, cons
 //   codes as two contiguous 64-byte runs.
 //   Call j = 0..3 takes column n0 + 4c + j (a lane holds two whole (gate, up)
 //   pairs); the token operand is 16 rows of x (or h) codes gathered in the
-//   same K order.  Weight loads run two steps ahead in a ring of three
-//   register sets (32 bytes per lane and column a step: a deeper ring would
-//   leave one wave per SIMD), token rows (L2-resident) one step ahead.
+//   same K order, token rows (L2-resident) one step ahead.
+//   Weight loads are line-coalesced instead (eight lanes per 128-byte line:
+//   load i, lane L reads 16 codes of column 8i + L/8 at K offset 16 (L%8)),
+//   two steps ahead in a ring of three register sets; each step writes its
+//   set into the wave's own 8 KB LDS slab and reads back the MFMA operand
+//   layout.  Slab address of (column, 16-byte piece p): column * 128 +
+//   16 (p ^ ((column / 4) % 8)), which keeps the writes free of bank
+//   conflicts and the operand reads at most two-way.
 // ---------------------------------------------------------------------------
 constexpr int kF8Waves = 4;
 constexpr int kF8NJ = 4;                 // columns per lane
@@ -509,7 +514,7 @@ constexpr int kF8Cols = 16 * kF8NJ;      // 64 columns per workgroup
 constexpr int kF8BK = 128;               // codes per K step
 
 struct F8W {
-  u32x4_t w[kF8NJ][2];
+  u32x4_t w[8];
 };
 template <int MG>
 struct F8A {
@@ -528,6 +533,7 @@ void gemv_fp8_kernel(
     const int32_t* __restrict__ rows,     // gate_up only: permuted slot ids
     int K, int N, int kslots, int a_rows, void* __restrict__ out) {
   __shared__ float red[kF8Waves][kF8NJ][4][kWave];   // 16 KB: one 16-row chunk's partial sums per wave
+  __shared__ __align__(16) u32x4_t slab[kF8Waves][kF8Cols * 8];   // 32 KB: each wave's staged weight step
 
   const int e = blockIdx.y;
   const int M = cnt[e];
@@ -543,9 +549,26 @@ void gemv_fp8_kernel(
 
   const rsrc_t w_rs = make_rsrc(Wq + (size_t)e * N * K, (uint32_t)N * (uint32_t)K);
   const rsrc_t a_rs = make_rsrc(A, (uint32_t)((size_t)a_rows * K));
-  uint32_t w_off[kF8NJ];
+  // coalesced weight loads: load i covers slab columns 8i .. 8i+7
+  const int wl_col = lane >> 3, wl_p = lane & 7;
+  uint32_t w_off[8];
+  int w_dst[8];
 #pragma unroll
-  for (int j = 0; j < kF8NJ; ++j) w_off[j] = (uint32_t)min(ncol + j, N - 1) * (uint32_t)K + 16u * g;
+  for (int i = 0; i < 8; ++i) {
+    const int col = 8 * i + wl_col;
+    w_off[i] = (uint32_t)min(blockIdx.x * kF8Cols + col, N - 1) * (uint32_t)K + 16u * wl_p;
+    w_dst[i] = col * 8 + (wl_p ^ ((col >> 2) & 7));
+  }
+  // operand reads: call j, half h of lane (c, g) = column 4c + j, piece 4h + g
+  int r_src[kF8NJ][2];
+#pragma unroll
+  for (int j = 0; j < kF8NJ; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int col = 4 * c + j;
+      r_src[j][h] = col * 8 + ((4 * h + g) ^ ((col >> 2) & 7));
+    }
+  u32x4_t* const my_slab = slab[wave];
   const int nk = (K + kF8BK - 1) / kF8BK;
   const int kb_begin = (nk * wave) / kF8Waves;
   const int kb_end = (nk * (wave + 1)) / kF8Waves;
@@ -569,13 +592,10 @@ void gemv_fp8_kernel(
     // loads of step q; steps outside this wave's range and pieces past K
     // read 0 (sent outside the descriptors, no memory touched)
     auto load_w = [&](int q, F8W& d) {
+      const uint32_t kb = (uint32_t)(q * kF8BK);
+      const bool in = q < kb_end && (int)kb + 16 * wl_p < K;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t kb = (uint32_t)(q * kF8BK + 64 * h);
-        const bool in = q < kb_end && (int)kb + 16 * g < K;
-#pragma unroll
-        for (int j = 0; j < kF8NJ; ++j) d.w[j][h] = buf_ld16(w_rs, in ? w_off[j] + kb : kOutOfRange);
-      }
+      for (int i = 0; i < 8; ++i) d.w[i] = buf_ld16(w_rs, in ? w_off[i] + kb : kOutOfRange);
     };
     auto load_a = [&](int q, F8A<MG>& d) {
 #pragma unroll
@@ -587,12 +607,23 @@ void gemv_fp8_kernel(
       }
     };
     auto step = [&](const F8W& dw, const F8A<MG>& da) {
+      // stage through the slab (a wave's LDS accesses complete in order, so
+      // the reads see this step's writes; the next step's writes follow the
+      // reads' data arriving in registers)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) my_slab[w_dst[i]] = dw.w[i];
+      u32x4_t bw[kF8NJ][2];
 #pragma unroll
       for (int j = 0; j < kF8NJ; ++j) {
-        acc[0][j] = mfma_fp8_16(da.a[0], dw.w[j], acc[0][j]);
+        bw[j][0] = my_slab[r_src[j][0]];
+        bw[j][1] = my_slab[r_src[j][1]];
+      }
+#pragma unroll
+      for (int j = 0; j < kF8NJ; ++j) {
+        acc[0][j] = mfma_fp8_16(da.a[0], bw[j], acc[0][j]);
         if (MG > 1 && nch > 1) {
 #pragma unroll
-          for (int qq = 1; qq < MG; ++qq) acc[qq][j] = mfma_fp8_16(da.a[qq], dw.w[j], acc[qq][j]);
+          for (int qq = 1; qq < MG; ++qq) acc[qq][j] = mfma_fp8_16(da.a[qq], bw[j], acc[qq][j]);
         }
       }
     };
