@@ -90,22 +90,31 @@ __global__ __launch_bounds__(kQThreads) void mxfp4_quantize_kernel(const bf16_t*
 }
 
 // ---------------------------------------------------------------------------
-// Weight-streaming expert kernel.  One wave per workgroup owns one expert and
-// a slice of 64 output columns over the whole of K, so its partial sums never
-// leave the registers.  K is walked in steps of four 32-value blocks (128 K).
-// Lane (g = lane/16, c = lane%16), call j = 0..3, reads block 4q+g of column
-// n0+4c+j: 16 bytes, the whole block.  The four 8-value quarters t of that
-// block are the B operands of four v_mfma_f32_16x16x32_bf16 calls, K index
-// 32(4q+g) + 8t + i in MFMA K slot (g, i); the token operand is loaded in the
-// same order (lane (row, g), 16 bytes of x at K = 32(4q+g) + 8t).  MFMA
-// column c of call j is weight column n0+4c+j, so gate and up of one pair
-// (calls j, j+1) sit in the same lane.  The scales of the lane's four columns
-// for its block are one 4-byte load (scales are block-major).  The
-// dequantisation is v_cvt_scalef32_pk_bf16_fp4 (two codes per instruction,
-// exact for every scale).  The weight loads run three steps ahead in a ring
-// of four register sets (the bytes in flight are what the streaming rate
-// depends on); the token rows come from L2 and run one step ahead.
+// Weight-streaming expert kernel.  A workgroup owns one expert and a slice of
+// 64 output columns; its four waves split K and stream their part straight
+// from HBM; the four partial sums are added in LDS in a fixed order.  K is
+// walked in double steps of eight 32-value blocks (256 K, one 128-byte line
+// of each column).
+//   Operands: lane (g = lane/16, c = lane%16), call j = 0..3, uses block
+//   8d + 4u + g (u = 0, 1) of column n0+4c+j in double step d: 16 bytes, the
+//   whole block, whose four 8-value quarters t are the B operands of four
+//   v_mfma_f32_16x16x32_bf16 calls, K index 32(8d+4u+g) + 8t + i in MFMA K
+//   slot (g, i); the token operand is loaded in the same order (lane (row,
+//   g), 16 bytes of x at K = 32(8d+4u+g) + 8t).  MFMA column c of call j is
+//   weight column n0+4c+j, so gate and up of one pair (calls j, j+1) sit in
+//   the same lane.  The scales of the lane's four columns for a block are one
+//   4-byte load (scales are block-major); v_cvt_scalef32_pk_bf16_fp4
+//   dequantises two codes per instruction, exactly for every scale.
+//   Weight loads are line-coalesced instead of operand-shaped (eight lanes
+//   per 128-byte line: load i, lane L reads block 8d + L%8 of column 8i +
+//   L/8), two double steps ahead in a ring of three register sets (with the
+//   scales of the same double step; the token rows, from L2, run one 128-K
+//   half step ahead in a pair of register sets); each double step
+//   writes its codes into the wave's own 8 KB LDS slab and reads back the
+//   operand layout.  Slab address of (column, block piece p): column * 128 +
+//   16 (p ^ ((column / 4) % 8)): conflict-free writes, at most two-way reads.
 // ---------------------------------------------------------------------------
+constexpr int kMxWaves = 4;
 constexpr int kMxNJ = 4;                 // columns per lane (calls j)
 constexpr int kMxCols = 16 * kMxNJ;      // 64 columns per workgroup
 constexpr int64_t kMxOneChunkMeanRows = 10;
@@ -130,17 +139,21 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t w, float s) {
                  __builtin_bit_cast(uint32_t, d)};
 }
 
-struct MxW {
-  u32x4_t w[kMxNJ];   // block 4q+g of the lane's columns
-  uint32_t s;         // their four scale bytes
+// one double step's weight loads: 8 coalesced code pieces and the scales of
+// the lane's two blocks (u = 0, 1)
+struct MxSlot {
+  u32x4_t w[8];
+  uint32_t s[2];
 };
+// the token pieces of one half step (block 4q + g)
 template <int MG>
 struct MxA {
-  u32x4_t a[MG][4];   // token rows: 16 bytes at K = 32(4q+g) + 8t
+  u32x4_t a[MG][4];
 };
 
 template <bool GATE_UP, int MG>
-__global__ __launch_bounds__(kWave) void gemv_mxfp4_kernel(
+__global__ __launch_bounds__(kMxWaves * kWave) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 2 : 1)))
+void gemv_mxfp4_kernel(
     const bf16_t* __restrict__ A,        // gate_up: x [T][K]; down: h [S][K] in permuted order
     const uint8_t* __restrict__ Wq,      // [E][N][K/2]
     const uint8_t* __restrict__ Ws,      // [E][K/32][N]
@@ -148,12 +161,16 @@ __global__ __launch_bounds__(kWave) void gemv_mxfp4_kernel(
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ off,
     const int32_t* __restrict__ rows,    // gate_up only: permuted slot ids
     int K, int N, int kslots, int a_rows, void* __restrict__ out) {
+  __shared__ float red[kMxWaves][kMxNJ][4][kWave];              // 16 KB: one chunk's partial sums per wave
+  __shared__ __align__(16) u32x4_t slab[kMxWaves][kMxCols * 8];  // 32 KB: each wave's staged double step
+
   const int e = blockIdx.y;
   const int M = cnt[e];
-  if (M == 0) return;   // the whole (one-wave) workgroup: no load for an expert without rows
+  if (M == 0) return;   // block-uniform: no load, no barrier for an expert without rows
   const int row0 = off[e];
   const int nblk = K / 32;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = lane >> 4;
   const int c = lane & 15;
   // N % 8 == 0 and ncol % 4 == 0: a lane's four columns are all in range or all out
@@ -164,14 +181,33 @@ __global__ __launch_bounds__(kWave) void gemv_mxfp4_kernel(
   const rsrc_t w_rs = make_rsrc(Wq + (size_t)e * N * row_bytes, (uint32_t)N * row_bytes);
   const rsrc_t s_rs = make_rsrc(Ws + (size_t)e * nblk * N, (uint32_t)(nblk * N));
   const rsrc_t a_rs = make_rsrc(A, (uint32_t)((size_t)a_rows * K * 2));
-  uint32_t w_off[kMxNJ];
-#pragma unroll
-  for (int j = 0; j < kMxNJ; ++j) w_off[j] = (uint32_t)min(ncol + j, N - 1) * row_bytes;
   const uint32_t s_col = (uint32_t)min(ncol, N - kMxNJ);
-  const int nq = (nblk + 3) / 4;
+  // coalesced code loads: load i covers slab columns 8i .. 8i+7
+  const int wl_col = lane >> 3, wl_p = lane & 7;
+  uint32_t w_off[8];
+  int w_dst[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int col = 8 * i + wl_col;
+    w_off[i] = (uint32_t)min(blockIdx.x * kMxCols + col, N - 1) * row_bytes + 16u * wl_p;
+    w_dst[i] = col * 8 + (wl_p ^ ((col >> 2) & 7));
+  }
+  // operand reads: call j, block u of lane (c, g) = column 4c + j, piece 4u + g
+  int r_src[kMxNJ][2];
+#pragma unroll
+  for (int j = 0; j < kMxNJ; ++j)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int col = 4 * c + j;
+      r_src[j][u] = col * 8 + ((4 * u + g) ^ ((col >> 2) & 7));
+    }
+  u32x4_t* const my_slab = slab[wave];
+  const int nds = (nblk + 7) / 8;
+  const int ds_begin = (nds * wave) / kMxWaves;
+  const int ds_end = (nds * (wave + 1)) / kMxWaves;
 
   for (int r0 = 0; r0 < M; r0 += 16 * MG) {
-    const int nch = min(MG, (M - r0 + 15) / 16);   // uniform
+    const int nch = min(MG, (M - r0 + 15) / 16);   // block-uniform
     uint32_t a_off[MG];
 #pragma unroll
     for (int qq = 0; qq < MG; ++qq) {
@@ -185,106 +221,122 @@ __global__ __launch_bounds__(kWave) void gemv_mxfp4_kernel(
 #pragma unroll
       for (int j = 0; j < kMxNJ; ++j) acc[qq][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // loads of step q; a block past K reads 0 (sent outside the descriptors)
-    auto load_w = [&](int q, MxW& d) {
-      const int b = 4 * q + g;
-      const bool in = b < nblk;
+    // loads of double step d (weights) and half step q (tokens); steps
+    // outside this wave's range and blocks past K read 0 (sent outside the
+    // descriptors, no memory touched)
+    auto load = [&](int d, MxSlot& sl) {
+      const bool w_in = d < ds_end && 8 * d + wl_p < nblk;
 #pragma unroll
-      for (int j = 0; j < kMxNJ; ++j) d.w[j] = buf_ld16(w_rs, in ? w_off[j] + 16u * b : kOutOfRange);
-      d.s = __builtin_amdgcn_raw_buffer_load_b32(s_rs, (int)(in ? (uint32_t)b * N + s_col : kOutOfRange), 0, 0);
+      for (int i = 0; i < 8; ++i) sl.w[i] = buf_ld16(w_rs, w_in ? w_off[i] + 128u * d : kOutOfRange);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int b = 8 * d + 4 * u + g;
+        const bool in = d < ds_end && b < nblk;
+        sl.s[u] = __builtin_amdgcn_raw_buffer_load_b32(s_rs, (int)(in ? (uint32_t)b * N + s_col : kOutOfRange), 0, 0);
+      }
     };
-    auto load_a = [&](int q, MxA<MG>& d) {
+    auto load_a = [&](int q, MxA<MG>& da) {
       const int b = 4 * q + g;
-      const bool in = b < nblk;
+      const bool in = q < 2 * ds_end && b < nblk;
 #pragma unroll
       for (int qq = 0; qq < MG; ++qq)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          d.a[qq][t] = buf_ld16(a_rs, in ? a_off[qq] + (uint32_t)(32 * b + 8 * t) * 2u : kOutOfRange);
+          da.a[qq][t] = buf_ld16(a_rs, in ? a_off[qq] + (uint32_t)(32 * b + 8 * t) * 2u : kOutOfRange);
     };
-    auto step = [&](const MxW& dw, const MxA<MG>& da) {
-      float sc[kMxNJ];
-#pragma unroll
-      for (int j = 0; j < kMxNJ; ++j) sc[j] = ue8m0_to_f32((dw.s >> (8 * j)) & 0xFF);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int j = 0; j < kMxNJ; ++j) {
-          const u32x4_t bw = dequant8(dw.w[j][t], sc[j]);
-          acc[0][j] = mfma16x16x32(da.a[0][t], bw, acc[0][j]);
-          if (MG > 1 && nch > 1) {
-#pragma unroll
-            for (int qq = 1; qq < MG; ++qq) acc[qq][j] = mfma16x16x32(da.a[qq][t], bw, acc[qq][j]);
-          }
-        }
-    };
-
-    MxW w0, w1, w2, w3;
     MxA<MG> a0, a1;
-    load_w(0, w0);
-    load_w(1, w1);
-    load_w(2, w2);
-    load_a(0, a0);
-    int q = 0;
-    for (; q + 4 <= nq; q += 4) {
-      load_w(q + 3, w3);
-      load_a(q + 1, a1);
-      step(w0, a0);
-      load_w(q + 4, w0);
-      load_a(q + 2, a0);
-      step(w1, a1);
-      load_w(q + 5, w1);
-      load_a(q + 3, a1);
-      step(w2, a0);
-      load_w(q + 6, w2);
-      load_a(q + 4, a0);
-      step(w3, a1);
-    }
-    // 0..3 steps left; w0, w1, w2 hold steps q, q+1, q+2 and a0 holds step q
-    if (q < nq) {
-      load_a(q + 1, a1);
-      step(w0, a0);
-    }
-    if (q + 1 < nq) {
-      load_a(q + 2, a0);
-      step(w1, a1);
-    }
-    if (q + 2 < nq) step(w2, a0);
-
-    // epilogue: 16x16 accumulator layout, lane (c, g) element v holds row
-    // 4g + v of MFMA column c = weight column ncol + j of call j
-    if (col_ok) {
-      float bb[kMxNJ];
-      {
-        // two 4-byte reads: the bias is only guaranteed 4-byte alignment
-        const uint32_t* bp = reinterpret_cast<const uint32_t*>(bias + (size_t)e * N + ncol);
-        const uint32_t b01 = bp[0], b23 = bp[1];
-        bb[0] = bf16lo(b01);
-        bb[1] = bf16hi(b01);
-        bb[2] = bf16lo(b23);
-        bb[3] = bf16hi(b23);
-      }
+    // double step d: half step u = 0 uses a0 (and loads a1 with half step
+    // 2d+1), u = 1 uses a1 (and loads a0 with 2d+2)
+    auto step = [&](int d, const MxSlot& sl) {
+      // stage the codes through the slab (a wave's LDS accesses complete in
+      // order: the reads see this step's writes, the next step's writes come
+      // after these reads)
 #pragma unroll
-      for (int qq = 0; qq < MG; ++qq) {
-        if (qq < nch) {
+      for (int i = 0; i < 8; ++i) my_slab[w_dst[i]] = sl.w[i];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int m = r0 + 16 * qq + 4 * g + v;
-            if (m < M) {
-              const size_t orow = (size_t)(row0 + m);
-              if (GATE_UP) {
-                const float h0 = clamped_glu(acc[qq][0][v] + bb[0], acc[qq][1][v] + bb[1]);
-                const float h1 = clamped_glu(acc[qq][2][v] + bb[2], acc[qq][3][v] + bb[3]);
-                *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + orow * (N / 2) + ncol / 2) =
-                    pack_bf16x2(h0, h1);
-              } else {
-                *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + orow * N + ncol) =
-                    f32x4_t{acc[qq][0][v] + bb[0], acc[qq][1][v] + bb[1], acc[qq][2][v] + bb[2],
-                            acc[qq][3][v] + bb[3]};
-              }
+      for (int u = 0; u < 2; ++u) {
+        const MxA<MG>& ac = u == 0 ? a0 : a1;
+        load_a(2 * d + u + 1, u == 0 ? a1 : a0);
+        u32x4_t bw[kMxNJ];
+#pragma unroll
+        for (int j = 0; j < kMxNJ; ++j) bw[j] = my_slab[r_src[j][u]];
+        float sc[kMxNJ];
+#pragma unroll
+        for (int j = 0; j < kMxNJ; ++j) sc[j] = ue8m0_to_f32((sl.s[u] >> (8 * j)) & 0xFF);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int j = 0; j < kMxNJ; ++j) {
+            const u32x4_t bq = dequant8(bw[j][t], sc[j]);
+            acc[0][j] = mfma16x16x32(ac.a[0][t], bq, acc[0][j]);
+            if (MG > 1 && nch > 1) {
+#pragma unroll
+              for (int qq = 1; qq < MG; ++qq) acc[qq][j] = mfma16x16x32(ac.a[qq][t], bq, acc[qq][j]);
             }
           }
+      }
+    };
+
+    MxSlot s0, s1, s2;
+    load(ds_begin, s0);
+    load_a(2 * ds_begin, a0);
+    load(ds_begin + 1, s1);
+    int d = ds_begin;
+    for (; d + 3 <= ds_end; d += 3) {
+      load(d + 2, s2);
+      step(d, s0);
+      load(d + 3, s0);
+      step(d + 1, s1);
+      load(d + 4, s1);
+      step(d + 2, s2);
+    }
+    // 0..2 double steps left; s0, s1 hold d, d+1 and a0 holds half step 2d
+    if (d < ds_end) step(d, s0);
+    if (d + 1 < ds_end) step(d + 1, s1);
+
+    // Sum the four K partials (fixed order: wave 0, 1, 2, 3); wave w then
+    // finishes accumulator element v = w (row 4g + w of each chunk) of all
+    // four columns.
+    float bb[kMxNJ];
+    {
+      // two 4-byte reads: the bias is only guaranteed 4-byte alignment
+      const uint32_t* bp = reinterpret_cast<const uint32_t*>(bias + (size_t)e * N + s_col);
+      const uint32_t b01 = bp[0], b23 = bp[1];
+      bb[0] = bf16lo(b01);
+      bb[1] = bf16hi(b01);
+      bb[2] = bf16lo(b23);
+      bb[3] = bf16hi(b23);
+    }
+#pragma unroll
+    for (int qq = 0; qq < MG; ++qq) {
+      if (qq < nch) {
+#pragma unroll
+        for (int j = 0; j < kMxNJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[qq][j][v];
+        __syncthreads();
+        float sum[kMxNJ];
+#pragma unroll
+        for (int j = 0; j < kMxNJ; ++j) {
+          float t = 0.f;
+#pragma unroll
+          for (int w2 = 0; w2 < kMxWaves; ++w2) t += red[w2][j][wave][lane];
+          sum[j] = t;
         }
+        const int m = r0 + 16 * qq + 4 * g + wave;
+        if (m < M && col_ok) {
+          const size_t orow = (size_t)(row0 + m);
+          if (GATE_UP) {
+            const float h0 = clamped_glu(sum[0] + bb[0], sum[1] + bb[1]);
+            const float h1 = clamped_glu(sum[2] + bb[2], sum[3] + bb[3]);
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + orow * (N / 2) + ncol / 2) =
+                pack_bf16x2(h0, h1);
+          } else {
+            *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + orow * N + ncol) =
+                f32x4_t{sum[0] + bb[0], sum[1] + bb[1], sum[2] + bb[2], sum[3] + bb[3]};
+          }
+        }
+        __syncthreads();
       }
     }
   }
@@ -300,7 +352,8 @@ hipError_t launch_mx(const void* A, const void* Wq, const void* Ws, const void* 
   dim3 grid((unsigned)((N + kMxCols - 1) / kMxCols), (unsigned)E);
   const bool one = T * k <= kMxOneChunkMeanRows * E;
   auto kern = one ? gemv_mxfp4_kernel<GATE_UP, 1> : gemv_mxfp4_kernel<GATE_UP, 2>;
-  hipLaunchKernelGGL(kern, grid, dim3(kWave), 0, stream, (const bf16_t*)A, (const uint8_t*)Wq, (const uint8_t*)Ws,
+  hipLaunchKernelGGL(kern, grid, dim3(kMxWaves * kWave), 0, stream, (const bf16_t*)A, (const uint8_t*)Wq,
+                     (const uint8_t*)Ws,
                      (const bf16_t*)bias, cnt, off, rows, K, N, GATE_UP ? k : 1, (int)a_rows, out);
   return hipGetLastError();
 }
