@@ -166,9 +166,10 @@ def _per_step_us(torch, step, stream, n, before=None):
 
 
 def _achievable(torch):
-    """What plain library kernels reach on this GPU right now, as context for
-    the roofline fractions (which use the published peaks): a 1 GiB
-    device-to-device copy and a bf16 8192^3 torch.matmul (hipBLASLt)."""
+    """What plain kernels reach on this GPU right now, as context for the
+    roofline fractions (which use the published peaks): the library's
+    hand-written streaming-read and MFMA probes, a 1 GiB device-to-device
+    copy and a bf16 8192^3 torch.matmul (hipBLASLt)."""
     import numpy as np
 
     def timed(fn, reps=5):
@@ -185,16 +186,28 @@ def _achievable(torch):
             ts.append(a.elapsed_time(b) * 1e-3)
         return float(np.median(ts))
 
+    from moe_layer_route_amd import binding
+
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     t_copy = timed(lambda: dst.copy_(src))
-    del src, dst
+    # hand-written streaming-read probe over the same 1 GiB (8192 workgroups of 128 KiB)
+    rd = torch.empty(8192 * 4, dtype=torch.int32, device="cuda")
+    t_read = timed(lambda: binding.probe_read(src, 8192, out=rd))
+    del src, dst, rd
+    # hand-written MFMA probe: 1024 workgroups x 4 waves x 4096 x 8 MFMAs 32x32x16 bf16
+    mo = torch.empty(1024 * 4, dtype=torch.float32, device="cuda")
+    t_mfma = timed(lambda: binding.probe_mfma_bf16(4096, 1024, out=mo))
+    mfma_ok = bool((mo == 2048.0 * 4096).all().item())
+    del mo
     n = 8192
     a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
     b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
     t_mm = timed(lambda: torch.matmul(a, b))
     del a, b
-    return {"copy_1GiB_GBs": 2 * (1 << 30) / t_copy / 1e9, "matmul_bf16_8192_TFLOPs": 2 * n ** 3 / t_mm / 1e12}
+    return {"copy_1GiB_GBs": 2 * (1 << 30) / t_copy / 1e9, "matmul_bf16_8192_TFLOPs": 2 * n ** 3 / t_mm / 1e12,
+            "probe_read_1GiB_GBs": (1 << 30) / t_read / 1e9,
+            "probe_mfma_bf16_TFLOPs": 1024 * 4 * 4096 * 8 * 32768 / t_mfma / 1e12, "probe_mfma_check": mfma_ok}
 
 
 def main(argv=None):

@@ -426,6 +426,30 @@ MOE_API int moe_down_fp8(const void* hq, const float* sh, const void* Wd_q, cons
                          int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, float* o,
                          int32_t path, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement probes.  They are not part of the block: they measure what a
+ * plain hand-written kernel gets from the matrix cores and from HBM on this
+ * GPU, the "achievable" context printed next to the roofline fractions (which
+ * use the published peaks).  Both are asynchronous on stream; time them with
+ * events around the call.
+ * ------------------------------------------------------------------------- */
+
+/* moe_probe_mfma_bf16 -- workgroups x 4 waves, each wave iters rounds of
+ * eight independent 32x32x16 bf16 MFMAs on all-ones operands:
+ * workgroups * 4 * iters * 8 * 32768 flops.
+ *   out float [workgroups * 4] (device, caller-owned): one value per wave,
+ *       exactly 2048 * iters when iters <= 8191 (a check of the result).
+ * iters in [1, 2^20), workgroups in [1, 65535]. */
+MOE_API int moe_probe_mfma_bf16(int32_t iters, int32_t workgroups, float* out, void* stream);
+
+/* moe_probe_read -- read buf (device, 16-byte aligned, bytes a multiple of
+ * 16) once with 16-byte loads, consecutive lanes on consecutive bytes, each
+ * workgroup one contiguous chunk of about bytes / workgroups.
+ *   out uint32 [workgroups * 4] (device, caller-owned): one XOR-fold per
+ *       wave; the XOR of all of them equals the XOR of buf's 32-bit words.
+ * workgroups in [1, 65535]; bytes = 0 writes zeros. */
+MOE_API int moe_probe_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

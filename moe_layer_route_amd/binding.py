@@ -27,7 +27,8 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace
            "moe_forward", "moe_forward_ex", "moe_forward_ep", "moe_permute", "moe_gate_up", "moe_down",
            "moe_combine", "moe_quantize_mxfp4", "moe_forward_mxfp4", "moe_forward_mxfp4_ex", "moe_gate_up_mxfp4",
            "moe_down_mxfp4", "moe_quantize_fp8", "moe_quantize_rows_fp8", "moe_workspace_bytes_fp8",
-           "moe_forward_fp8", "moe_forward_fp8_ex", "moe_gate_up_fp8", "moe_down_fp8", "moe_forward_padded")
+           "moe_forward_fp8", "moe_forward_fp8_ex", "moe_gate_up_fp8", "moe_down_fp8", "moe_forward_padded",
+           "moe_probe_mfma_bf16", "moe_probe_read")
 
 
 class MoEError(RuntimeError):
@@ -66,6 +67,8 @@ _SIGS = {
     "moe_forward_fp8_ex": (ctypes.c_int, [_vp] * 9 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _i32, _vp]),
     "moe_gate_up_fp8": (ctypes.c_int, [_vp] * 8 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
     "moe_down_fp8": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
+    "moe_probe_mfma_bf16": (ctypes.c_int, [_i32, _i32, _vp, _vp]),
+    "moe_probe_read": (ctypes.c_int, [_vp, _sz, _i32, _vp, _vp]),
 }
 
 
@@ -466,3 +469,28 @@ def moe_forward_padded(x, Wr, br, Wgu, bgu, Wd, bd, k: int = 4, n_valid=None, y=
                                       workspace.numel() * workspace.element_size(), path_code(path), _stream(stream))
     _check(st, "moe_forward_padded")
     return y
+
+
+# ---------------------------------------------------------------------------
+# measurement probes (not part of the block)
+# ---------------------------------------------------------------------------
+def probe_mfma_bf16(iters: int, workgroups: int, out=None, stream=None):
+    """Enqueue the MFMA rate probe; returns out (float32 [workgroups * 4], each
+    2048 * iters when iters <= 8191).  Flops = workgroups * 4 * iters * 8 * 32768."""
+    if out is None:
+        out = torch.empty(workgroups * 4, dtype=torch.float32, device="cuda")
+    _dev(out)
+    _check(library().moe_probe_mfma_bf16(iters, workgroups, _ptr(out), _stream(stream)), "moe_probe_mfma_bf16")
+    return out
+
+
+def probe_read(buf, workgroups: int, out=None, stream=None):
+    """Enqueue the streaming-read probe over buf (any dtype, contiguous, bytes % 16 == 0);
+    returns out (int32 [workgroups * 4] holding uint32 XOR folds)."""
+    _dev(buf)
+    if out is None:
+        out = torch.empty(workgroups * 4, dtype=torch.int32, device=buf.device)
+    _dev(out)
+    nbytes = buf.numel() * buf.element_size()
+    _check(library().moe_probe_read(_ptr(buf), nbytes, workgroups, _ptr(out), _stream(stream)), "moe_probe_read")
+    return out

@@ -73,6 +73,10 @@ hipError_t launch_gemv_fp8_down(const void* hq, const float* sh, const void* Wq,
                                 const int32_t* cnt, const int32_t* off, int64_t T, int H, int E, int k, int I,
                                 float* o, hipStream_t stream);
 
+// measurement probes (probe.hip)
+hipError_t launch_probe_mfma(int iters, int workgroups, float* out, hipStream_t stream);
+hipError_t launch_probe_read(const void* buf, size_t bytes, int workgroups, uint32_t* out, hipStream_t stream);
+
 // slots with pos < 0 are left out; out_f32: y is float32 (partial sums), else bf16
 hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, int64_t T, int H, int k,
                           void* y, hipStream_t stream, bool out_f32 = false);

@@ -714,6 +714,30 @@ int moe_down_fp8(const void* hq, const float* sh, const void* Wd_q, const float*
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// measurement probes
+// ---------------------------------------------------------------------------
+int moe_probe_mfma_bf16(int32_t iters, int32_t workgroups, float* out, void* stream) {
+  const char* fn = "moe_probe_mfma_bf16";
+  if (iters < 1 || iters >= (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "%s: iters=%d outside [1, 2^20)", fn, iters);
+  if (workgroups < 1 || workgroups > 65535)
+    return fail(MOE_ERR_INVALID_ARG, "%s: workgroups=%d outside [1, 65535]", fn, workgroups);
+  CHECK_PTR(out, 4);
+  if (int st = hip_status(fn, moe::launch_probe_mfma(iters, workgroups, out, (hipStream_t)stream))) return st;
+  return ok();
+}
+
+int moe_probe_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* out, void* stream) {
+  const char* fn = "moe_probe_read";
+  if (bytes % 16 != 0) return fail(MOE_ERR_INVALID_ARG, "%s: bytes=%zu is not a multiple of 16", fn, bytes);
+  if (workgroups < 1 || workgroups > 65535)
+    return fail(MOE_ERR_INVALID_ARG, "%s: workgroups=%d outside [1, 65535]", fn, workgroups);
+  if (bytes > 0) CHECK_PTR(buf, 16);
+  CHECK_PTR(out, 4);
+  if (int st = hip_status(fn, moe::launch_probe_read(buf, bytes, workgroups, out, (hipStream_t)stream))) return st;
+  return ok();
+}
+
 int moe_combine(const float* o, const int32_t* pos, const float* topk_w, int64_t T, int32_t H, int32_t k,
                 void* y, void* stream) {
   const char* fn = "moe_combine";

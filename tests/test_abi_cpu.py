@@ -224,3 +224,14 @@ def test_padded_calls_validate(lib):
     assert call(path=9) == INVALID and b"unknown path" in lib.moe_last_error()
     assert call(ws=16) == WORKSPACE
     assert call(T=0, n_valid=v, counts=v) == OK
+
+
+def test_probe_calls_validate(lib):
+    v = ctypes.c_void_p(FAKE)
+    assert lib.moe_probe_mfma_bf16(0, 4, v, None) == INVALID and b"iters" in lib.moe_last_error()
+    assert lib.moe_probe_mfma_bf16(1 << 20, 4, v, None) == INVALID
+    assert lib.moe_probe_mfma_bf16(16, 0, v, None) == INVALID and b"workgroups" in lib.moe_last_error()
+    assert lib.moe_probe_mfma_bf16(16, 4, None, None) == INVALID and b"out" in lib.moe_last_error()
+    assert lib.moe_probe_read(v, 24, 4, v, None) == INVALID and b"multiple of 16" in lib.moe_last_error()
+    assert lib.moe_probe_read(ctypes.c_void_p(FAKE + 8), 32, 4, v, None) == INVALID
+    assert lib.moe_probe_read(v, 32, 70000, v, None) == INVALID and b"workgroups" in lib.moe_last_error()
