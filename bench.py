@@ -127,9 +127,11 @@ def cpu_baseline(inp, k, min_seconds=10.0, max_reps=3, mx_arrays=None, f8_arrays
     import oracle.moe_oracle as orc
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        blas_pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max([i.get("num_threads", 1) for i in blas_pools] or [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in blas_pools})) or "unknown"
     except Exception:  # pragma: no cover
-        cores = 1
+        cores, blas = 1, "unknown"
     times = []
     t_all = time.perf_counter()
     while len(times) < max_reps and (time.perf_counter() - t_all) < min_seconds:
@@ -142,7 +144,7 @@ def cpu_baseline(inp, k, min_seconds=10.0, max_reps=3, mx_arrays=None, f8_arrays
             orc.moe_forward(*inp.arrays(), k=k)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
-    return {"value": inp.cfg.T / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": inp.cfg.T / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle", "blas": blas,
             "sample": f"whole {inp.cfg.name} batch (T={inp.cfg.T}) through the float64 numpy oracle"
                       f"{' (MXFP4 weights)' if mx_arrays is not None else ''}"
                       f"{' (FP8 W8A8)' if f8_arrays is not None else ''}, "
