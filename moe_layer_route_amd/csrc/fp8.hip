@@ -14,8 +14,8 @@
 // token's x row for gate_up, a (token, slot) row of h for down).  h is
 // rounded to bf16 by the gate_up epilogue and quantised by the row kernel.
 //
-// Tiled GEMM: the bf16 kernel's (expert, m-tile) lookup, XCD-aware order,
-// three-buffer token LDS ring and barrier placement, with
+// Tiled GEMM: the bf16 kernel's (expert, m-tile) lookup, XCD-aware order and
+// three-buffer token LDS ring (one barrier per step, at its start), with
 // v_mfma_f32_16x16x128_f8f6f4 on K steps of 128 codes.  A workgroup covers
 // 128 rows x 256 columns; each of its four waves 128 x 64 = 8 x 4 blocks of
 // 16 x 16 (128 accumulators per lane).
@@ -29,9 +29,13 @@
 //   requests).  Two steps ahead, in a ring of three register sets.
 //   A (codes of token rows): gathered through rows[] (gate_up) or contiguous
 //   (down); each thread copies four 16-byte pieces a step, eight threads per
-//   128-byte row, four steps ahead, into the fragment-major LDS ring two steps
+//   128-byte row, three steps ahead, into the fragment-major LDS ring two steps
 //   ahead: fragment mi (rows 16mi..16mi+15) holds, in lane order, the 32
-//   bytes lane l of the MFMA needs.
+//   bytes lane l of the MFMA needs.  A step reads its fragments back two MFMA
+//   groups before use into a ring of three: holding all eight fragments of a
+//   step (64 registers) pushed the register allocator into rotating the
+//   accumulators through spare registers every loop iteration, 72 moves each
+//   waiting on an MFMA result.
 // Epilogue: in the 16 x 16 accumulator layout lane l, element v holds row
 // 4*(l/16) + v of MFMA column l%16, i.e. weight column n0 + 64w + 4c + j of
 // block j: a lane holds two whole (gate, up) pairs.  Product * s_row *
@@ -353,75 +357,66 @@ __global__ __launch_bounds__(kFgThreads, 1) void gemm_fp8_kernel(
 
   // Registers (the loop is unrolled three times and no ring needs a register
   // copy): B of steps kt, kt+1, kt+2 (Rb[kt%3] is used by step kt and then
-  // reloaded, at step kt+1, with step kt+3); A of steps kt+2, kt+3 and kt+4
-  // (Ra[j%3] holds A(j) from its load, four steps ahead, to its LDS store,
-  // two steps ahead); the A fragments F of step kt (each reloaded with step
-  // kt+1 after its last MFMA).
+  // reloaded, at step kt+1, with step kt+3); A of steps kt+2 and kt+3
+  // (Ra[j%3] holds A(j) from its load, three steps ahead, to its LDS store,
+  // two steps ahead); a ring of three A fragments (fragment mi of a step in
+  // Fr[mi%3], read from LDS two groups before its MFMAs; the last two groups
+  // of a step read fragments 0 and 1 of the next).
   u32x4_t Rb[3][4][2];
   u32x4_t Ra[3][4];
-  u32x4_t F[8][2];
+  u32x4_t Fr[3][2];
 
-  // One K step kt (r = kt % 3): issue the loads of A(kt+4), then B(kt+2)
-  // (loads retire in order: a later store of A waits for A alone); multiply
-  // B(kt) with F, reading the fragments of kt+1 as those of kt retire; store
-  // A(kt+2); one barrier after the fifth of the eight MFMA groups.  The LDS
-  // ring: buffer (kt+1)%3 is read during step kt, buffer (kt+2)%3 written
-  // before its barrier (its previous reads, of step kt-2, all precede the
-  // barrier of step kt-1).
+  // One K step kt (r = kt % 3): a barrier; issue the loads of A(kt+3), then
+  // B(kt+2) (loads retire in order: a later store of A waits for A alone);
+  // multiply B(kt) with the fragments of buffer kt%3; store A(kt+2) into
+  // buffer (kt+2)%3 after the fourth group.  The barrier orders the previous
+  // step's reads of buffer (kt+2)%3 before this store, and the previous
+  // step's store into buffer (kt+1)%3 before this step's reads of it (its
+  // last two groups read the next step's first fragments).
   auto step = [&](int kt, auto rc) {
     constexpr int r = decltype(rc)::value;
     const u32x4_t (&bt)[4][2] = Rb[r];
     __builtin_amdgcn_sched_barrier(0);
-    gload_a(kt + 4, Ra[(r + 1) % 3]);
-    gload_b(kt + 2, Rb[(r + 2) % 3]);
-    const int nbuf = (kt + 1) % kFgLdsBufs;
-    auto group = [&](int mi) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[mi][j] = mfma_fp8_16(F[mi], bt[j], acc[mi][j]);
-    };
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      group(mi);
-      lread(nbuf, mi, F[mi]);
-    }
-    lstore(kt + 2, Ra[(r + 2) % 3]);
-    group(4);
-    // the twelve global loads over the first twenty MFMAs
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 global load
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // 2 LDS reads
-    }
-    __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);       // 4 LDS writes
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __syncthreads();
-    lread(nbuf, 4, F[4]);
+    gload_a(kt + 3, Ra[r]);
+    gload_b(kt + 2, Rb[(r + 2) % 3]);
+    const int cbuf = kt % kFgLdsBufs, nbuf = (kt + 1) % kFgLdsBufs;
 #pragma unroll
-    for (int mi = 5; mi < 8; ++mi) {
-      group(mi);
-      lread(nbuf, mi, F[mi]);
+    for (int mi = 0; mi < 8; ++mi) {
+      if (mi + 2 < 8) lread(cbuf, mi + 2, Fr[(mi + 2) % 3]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[mi][j] = mfma_fp8_16(Fr[mi % 3], bt[j], acc[mi][j]);
+      if (mi == 3) lstore(kt + 2, Ra[(r + 2) % 3]);
+      if (mi >= 6) lread(nbuf, mi - 6, Fr[mi % 3]);
+    }
+    // the twelve global loads over the first six groups; each fragment read
+    // two groups ahead of its MFMAs
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+      if (mi < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // 1 MFMA
+      if (mi < 6) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 global load
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (mi < 6) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (mi == 3) __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);  // 4 LDS writes
+      if (mi >= 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
 
-  // Prologue: the loads in the order the steps issue them (A(j+2), then
-  // B(j)), so the wait counts of the first steps match the later ones.
+  // Prologue: the loads in the order the steps issue them (A(j+3), then
+  // B(j+2)), so the wait counts of the first steps match the later ones.
   const int nk = (K + kFgBK - 1) / kFgBK;
   gload_a(0, Ra[0]);
   gload_a(1, Ra[1]);
-  gload_a(2, Ra[2]);
   gload_b(0, Rb[0]);
   lstore(0, Ra[0]);
-  gload_a(3, Ra[0]);
+  gload_a(2, Ra[2]);
   gload_b(1, Rb[1]);
   lstore(1, Ra[1]);
   __syncthreads();
-#pragma unroll
-  for (int mi = 0; mi < 8; ++mi) lread(0, mi, F[mi]);
+  lread(0, 0, Fr[0]);
+  lread(0, 1, Fr[1]);
 
   // The step count is rounded up to the unroll period: an extra step reads
   // only zeros (K past the end on both operands) and adds exactly 0.
