@@ -162,6 +162,9 @@ SWEEP = [
     (257, 8, 136, 128, 2),
     (40, 4, 128, 2888, 1),
     (3, 4, 16384, 40, 2),      # largest H: many K steps / chunk groups
+    (3, 4, 40, 16384, 2),      # largest I: 2I = 32768 gate_up columns, K = 16384 for down
+    (50, 256, 136, 72, 8),     # largest E and k
+    (2000, 256, 136, 72, 8),   # largest E and k with a mean load above the tiled path's threshold
 ]
 
 
