@@ -111,6 +111,8 @@ def test_quantize_rows_matches_oracle(R, K):
     (17, 32, 2880, 2880, 4),  # full hidden and intermediate sizes
     (9, 40, 2880, 224, 8),    # k = 8, E not a power of two, empty experts
     (257, 8, 2880, 2880, 2),  # ragged M tiles at full size
+    (60, 256, 128, 96, 8),    # largest E and k
+    (1700, 256, 128, 96, 8),  # largest E and k, mean load above the tiled path's threshold
 ])
 @pytest.mark.parametrize("path", PATHS)
 def test_forward_sweep(T, E, H, I, k, path):

@@ -93,6 +93,8 @@ def test_quantize_matches_oracle(E, K, N):
     (9, 40, 2880, 224, 8),    # k = 8, E not a power of two, empty experts
     (300, 4, 160, 608, 4),    # 300 rows per expert: three 128-row tiles; K = 160 is 1.25 quads
     (257, 8, 2880, 2880, 2),  # ragged M tiles at full size
+    (60, 256, 128, 96, 8),    # largest E and k
+    (1700, 256, 128, 96, 8),  # largest E and k, mean load above the tiled path's threshold
 ])
 @pytest.mark.parametrize("path", PATHS)
 def test_forward_sweep(T, E, H, I, k, path):
