@@ -250,7 +250,7 @@ MOE_API int moe_combine(const float* o, const int32_t* pos, const float* topk_w,
  * (static buffers, pad tails zeroed for determinism) and the Phase 19 page's
  * per-layer expert-load recorder are the callers this serves.
  *   n_valid            device int32 (nullable: every row valid), read on the
- *                      device when the call runs, clamped to [0, T): rows
+ *                      device when the call runs, clamped to [0, T]: rows
  *                      t >= n_valid are padding.  A padding row is routed to no
  *                      expert (topk_ids -1, topk_w 0), costs no expert work,
  *                      and its y row is 0.  Grids are sized from T alone, so a
@@ -265,6 +265,27 @@ MOE_API int moe_forward_padded(const void* x, const void* Wr, const void* br,
                                const int32_t* n_valid, void* y, int32_t* topk_ids_out, float* topk_w_out,
                                int32_t* expert_counts_out, void* workspace, size_t workspace_bytes,
                                int32_t path, void* stream);
+
+/* moe_forward_padded_mxfp4, moe_forward_padded_fp8 -- moe_forward_padded with
+ * MXFP4 or FP8 expert weights: the weight arguments, their formats and the
+ * workspace (moe_workspace_bytes, moe_workspace_bytes_fp8) are those of
+ * moe_forward_mxfp4_ex and moe_forward_fp8_ex; n_valid, expert_counts_out,
+ * the padding rows' outputs and every other argument are as in
+ * moe_forward_padded. */
+MOE_API int moe_forward_padded_mxfp4(const void* x, const void* Wr, const void* br,
+                                     const void* Wgu_q, const void* Wgu_s, const void* bgu,
+                                     const void* Wd_q, const void* Wd_s, const void* bd,
+                                     int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                                     const int32_t* n_valid, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                                     int32_t* expert_counts_out, void* workspace, size_t workspace_bytes,
+                                     int32_t path, void* stream);
+MOE_API int moe_forward_padded_fp8(const void* x, const void* Wr, const void* br,
+                                   const void* Wgu_q, const float* Wgu_s, const void* bgu,
+                                   const void* Wd_q, const float* Wd_s, const void* bd,
+                                   int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                                   const int32_t* n_valid, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                                   int32_t* expert_counts_out, void* workspace, size_t workspace_bytes,
+                                   int32_t path, void* stream);
 
 /*
  * MXFP4 expert weights (W4A16) -- xserv "Phase 19: gpt-oss-20b MoE support",

@@ -28,7 +28,7 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace
            "moe_combine", "moe_quantize_mxfp4", "moe_forward_mxfp4", "moe_forward_mxfp4_ex", "moe_gate_up_mxfp4",
            "moe_down_mxfp4", "moe_quantize_fp8", "moe_quantize_rows_fp8", "moe_workspace_bytes_fp8",
            "moe_forward_fp8", "moe_forward_fp8_ex", "moe_gate_up_fp8", "moe_down_fp8", "moe_forward_padded",
-           "moe_probe_mfma_bf16", "moe_probe_read")
+           "moe_probe_mfma_bf16", "moe_probe_read", "moe_forward_padded_mxfp4", "moe_forward_padded_fp8")
 
 
 class MoEError(RuntimeError):
@@ -67,6 +67,10 @@ _SIGS = {
     "moe_forward_fp8_ex": (ctypes.c_int, [_vp] * 9 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4 + [_sz, _i32, _vp]),
     "moe_gate_up_fp8": (ctypes.c_int, [_vp] * 8 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
     "moe_down_fp8": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
+    "moe_forward_padded_mxfp4": (ctypes.c_int, [_vp] * 9 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 5
+                                 + [_vp, _sz, _i32, _vp]),
+    "moe_forward_padded_fp8": (ctypes.c_int, [_vp] * 9 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 5
+                               + [_vp, _sz, _i32, _vp]),
     "moe_probe_mfma_bf16": (ctypes.c_int, [_i32, _i32, _vp, _vp]),
     "moe_probe_read": (ctypes.c_int, [_vp, _sz, _i32, _vp, _vp]),
 }
@@ -468,6 +472,63 @@ def moe_forward_padded(x, Wr, br, Wgu, bgu, Wd, bd, k: int = 4, n_valid=None, y=
                                       _ptr(expert_counts), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), path_code(path), _stream(stream))
     _check(st, "moe_forward_padded")
+    return y
+
+
+def _padded_args(n_valid, expert_counts, E):
+    if n_valid is not None and (n_valid.dtype != torch.int32 or n_valid.numel() != 1):
+        raise MoEError("n_valid must be a one-element int32 tensor")
+    if expert_counts is not None and (expert_counts.dtype != torch.int32 or expert_counts.numel() != E):
+        raise MoEError("expert_counts must be an int32 tensor of E elements")
+
+
+def moe_forward_padded_mxfp4(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k: int = 4, n_valid=None, y=None,
+                             workspace=None, topk_ids=None, topk_w=None, expert_counts=None, path="auto",
+                             stream=None):
+    """moe_forward_padded with MXFP4 expert weights; returns y (bf16 [T,H])."""
+    _dev(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd)
+    _b16(x, Wr, br, bgu, bd)
+    _u8(Wgu_q, Wgu_s, Wd_q, Wd_s)
+    T, H = x.shape
+    E = Wr.shape[0]
+    I = Wd_q.shape[2] * 2
+    _padded_args(n_valid, expert_counts, E)
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(T, H, E, k, I, x.device)
+    _dev(y, workspace, topk_ids, topk_w, n_valid, expert_counts)
+    st = library().moe_forward_padded_mxfp4(_ptr(x), _ptr(Wr), _ptr(br), _ptr(Wgu_q), _ptr(Wgu_s), _ptr(bgu),
+                                            _ptr(Wd_q), _ptr(Wd_s), _ptr(bd), T, H, E, k, I, _ptr(n_valid), _ptr(y),
+                                            _ptr(topk_ids), _ptr(topk_w), _ptr(expert_counts), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), path_code(path),
+                                            _stream(stream))
+    _check(st, "moe_forward_padded_mxfp4")
+    return y
+
+
+def moe_forward_padded_fp8(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k: int = 4, n_valid=None, y=None,
+                           workspace=None, topk_ids=None, topk_w=None, expert_counts=None, path="auto", stream=None):
+    """moe_forward_padded with FP8 W8A8 experts; returns y (bf16 [T,H])."""
+    _dev(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd)
+    _b16(x, Wr, br, bgu, bd)
+    _u8(Wgu_q, Wd_q)
+    _f32(Wgu_s, Wd_s)
+    T, H = x.shape
+    E = Wr.shape[0]
+    I = Wd_q.shape[2]
+    _padded_args(n_valid, expert_counts, E)
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace_fp8(T, H, E, k, I, x.device)
+    _dev(y, workspace, topk_ids, topk_w, n_valid, expert_counts)
+    st = library().moe_forward_padded_fp8(_ptr(x), _ptr(Wr), _ptr(br), _ptr(Wgu_q), _ptr(Wgu_s), _ptr(bgu),
+                                          _ptr(Wd_q), _ptr(Wd_s), _ptr(bd), T, H, E, k, I, _ptr(n_valid), _ptr(y),
+                                          _ptr(topk_ids), _ptr(topk_w), _ptr(expert_counts), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), path_code(path),
+                                          _stream(stream))
+    _check(st, "moe_forward_padded_fp8")
     return y
 
 

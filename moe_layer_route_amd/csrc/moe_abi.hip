@@ -421,11 +421,13 @@ static int run_down_mx(const char* fn, const void* h, const void* Wq, const void
   return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
 }
 
-int moe_forward_mxfp4_ex(const void* x, const void* Wr, const void* br, const void* Wgu_q, const void* Wgu_s,
-                         const void* bgu, const void* Wd_q, const void* Wd_s, const void* bd, int64_t T, int32_t H,
-                         int32_t E, int32_t k, int32_t I, void* y, int32_t* topk_ids_out, float* topk_w_out,
-                         void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
-  const char* fn = "moe_forward_mxfp4";
+// The MXFP4 forward; n_valid (device, optional) marks the rows from *n_valid
+// on as padding, expert_counts_out (optional) receives the per-expert loads.
+static int forward_mxfp4(const char* fn, const void* x, const void* Wr, const void* br, const void* Wgu_q,
+                         const void* Wgu_s, const void* bgu, const void* Wd_q, const void* Wd_s, const void* bd,
+                         int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, const int32_t* n_valid, void* y,
+                         int32_t* topk_ids_out, float* topk_w_out, int32_t* expert_counts_out, void* workspace,
+                         size_t workspace_bytes, int32_t path, void* stream) {
   if (int st = check_dims(fn, T, H, E, k, I)) return st;
   if (int st = check_mx_dims(fn, H, I)) return st;
   CHECK_PTR(x, 16);
@@ -442,6 +444,9 @@ int moe_forward_mxfp4_ex(const void* x, const void* Wr, const void* br, const vo
     return fail(MOE_ERR_INVALID_ARG, "%s: topk_ids_out is not 4-byte aligned", fn);
   if (topk_w_out && !aligned(topk_w_out, 4))
     return fail(MOE_ERR_INVALID_ARG, "%s: topk_w_out is not 4-byte aligned", fn);
+  if (n_valid && !aligned(n_valid, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: n_valid is not 4-byte aligned", fn);
+  if (expert_counts_out && !aligned(expert_counts_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s: expert_counts_out is not 4-byte aligned", fn);
   if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
     return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
   if (T == 0) return ok();
@@ -455,7 +460,7 @@ int moe_forward_mxfp4_ex(const void* x, const void* Wr, const void* br, const vo
   char* ws = static_cast<char*>(workspace);
   int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
   float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
-  int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.cnt);
+  int32_t* cnt = expert_counts_out ? expert_counts_out : reinterpret_cast<int32_t*>(ws + L.cnt);
   int32_t* off = reinterpret_cast<int32_t*>(ws + L.off);
   int32_t* rows = reinterpret_cast<int32_t*>(ws + L.rows);
   int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
@@ -464,11 +469,31 @@ int moe_forward_mxfp4_ex(const void* x, const void* Wr, const void* br, const vo
   hipStream_t s = (hipStream_t)stream;
 
   if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, ids, w, MOE_ROUTE_AUTO, s))) return st;
+  if (n_valid)
+    if (int st = hip_status(fn, moe::launch_mask_padding(ids, w, T, k, n_valid, s))) return st;
   if (int st = hip_status(fn, moe::launch_permute(ids, T, E, k, cnt, off, rows, pos, s))) return st;
   if (int st = run_gate_up_mx(fn, x, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, E, k, I, h, path, s)) return st;
   if (int st = run_down_mx(fn, h, Wd_q, Wd_s, bd, cnt, off, T, H, E, k, I, o, path, s)) return st;
   if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s))) return st;
   return ok();
+}
+
+int moe_forward_mxfp4_ex(const void* x, const void* Wr, const void* br, const void* Wgu_q, const void* Wgu_s,
+                         const void* bgu, const void* Wd_q, const void* Wd_s, const void* bd, int64_t T, int32_t H,
+                         int32_t E, int32_t k, int32_t I, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                         void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
+  return forward_mxfp4("moe_forward_mxfp4", x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, T, H, E, k, I, nullptr, y,
+                       topk_ids_out, topk_w_out, nullptr, workspace, workspace_bytes, path, stream);
+}
+
+int moe_forward_padded_mxfp4(const void* x, const void* Wr, const void* br, const void* Wgu_q, const void* Wgu_s,
+                             const void* bgu, const void* Wd_q, const void* Wd_s, const void* bd, int64_t T,
+                             int32_t H, int32_t E, int32_t k, int32_t I, const int32_t* n_valid, void* y,
+                             int32_t* topk_ids_out, float* topk_w_out, int32_t* expert_counts_out, void* workspace,
+                             size_t workspace_bytes, int32_t path, void* stream) {
+  return forward_mxfp4("moe_forward_padded_mxfp4", x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, T, H, E, k, I,
+                       n_valid, y, topk_ids_out, topk_w_out, expert_counts_out, workspace, workspace_bytes, path,
+                       stream);
 }
 
 int moe_forward_mxfp4(const void* x, const void* Wr, const void* br, const void* Wgu_q, const void* Wgu_s,
@@ -602,11 +627,13 @@ static int run_down_fp8(const char* fn, const void* hq, const float* sh, const v
   return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
 }
 
-int moe_forward_fp8_ex(const void* x, const void* Wr, const void* br, const void* Wgu_q, const float* Wgu_s,
-                       const void* bgu, const void* Wd_q, const float* Wd_s, const void* bd, int64_t T, int32_t H,
-                       int32_t E, int32_t k, int32_t I, void* y, int32_t* topk_ids_out, float* topk_w_out,
-                       void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
-  const char* fn = "moe_forward_fp8";
+// The FP8 forward; n_valid (device, optional) marks the rows from *n_valid on
+// as padding, expert_counts_out (optional) receives the per-expert loads.
+static int forward_fp8(const char* fn, const void* x, const void* Wr, const void* br, const void* Wgu_q,
+                       const float* Wgu_s, const void* bgu, const void* Wd_q, const float* Wd_s, const void* bd,
+                       int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, const int32_t* n_valid, void* y,
+                       int32_t* topk_ids_out, float* topk_w_out, int32_t* expert_counts_out, void* workspace,
+                       size_t workspace_bytes, int32_t path, void* stream) {
   if (int st = check_dims(fn, T, H, E, k, I)) return st;
   if (int st = check_fp8_dims(fn, H, I)) return st;
   CHECK_PTR(x, 16);
@@ -623,6 +650,9 @@ int moe_forward_fp8_ex(const void* x, const void* Wr, const void* br, const void
     return fail(MOE_ERR_INVALID_ARG, "%s: topk_ids_out is not 4-byte aligned", fn);
   if (topk_w_out && !aligned(topk_w_out, 4))
     return fail(MOE_ERR_INVALID_ARG, "%s: topk_w_out is not 4-byte aligned", fn);
+  if (n_valid && !aligned(n_valid, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: n_valid is not 4-byte aligned", fn);
+  if (expert_counts_out && !aligned(expert_counts_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s: expert_counts_out is not 4-byte aligned", fn);
   if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
     return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
   if (T == 0) return ok();
@@ -637,7 +667,7 @@ int moe_forward_fp8_ex(const void* x, const void* Wr, const void* br, const void
   const Layout& L = F.base;
   int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
   float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
-  int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.cnt);
+  int32_t* cnt = expert_counts_out ? expert_counts_out : reinterpret_cast<int32_t*>(ws + L.cnt);
   int32_t* off = reinterpret_cast<int32_t*>(ws + L.off);
   int32_t* rows = reinterpret_cast<int32_t*>(ws + L.rows);
   int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
@@ -651,6 +681,8 @@ int moe_forward_fp8_ex(const void* x, const void* Wr, const void* br, const void
   const int64_t S = T * k;
 
   if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, ids, w, MOE_ROUTE_AUTO, s))) return st;
+  if (n_valid)
+    if (int st = hip_status(fn, moe::launch_mask_padding(ids, w, T, k, n_valid, s))) return st;
   if (int st = hip_status(fn, moe::launch_permute(ids, T, E, k, cnt, off, rows, pos, s))) return st;
   if (int st = hip_status(fn, moe::launch_fp8_quantize_rows(x, T, H, xq, sx, s))) return st;
   if (int st = run_gate_up_fp8(fn, xq, sx, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, E, k, I, h, path, s)) return st;
@@ -658,6 +690,24 @@ int moe_forward_fp8_ex(const void* x, const void* Wr, const void* br, const void
   if (int st = run_down_fp8(fn, hq, sh, Wd_q, Wd_s, bd, cnt, off, T, H, E, k, I, o, path, s)) return st;
   if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s))) return st;
   return ok();
+}
+
+int moe_forward_fp8_ex(const void* x, const void* Wr, const void* br, const void* Wgu_q, const float* Wgu_s,
+                       const void* bgu, const void* Wd_q, const float* Wd_s, const void* bd, int64_t T, int32_t H,
+                       int32_t E, int32_t k, int32_t I, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                       void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
+  return forward_fp8("moe_forward_fp8", x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, T, H, E, k, I, nullptr, y,
+                     topk_ids_out, topk_w_out, nullptr, workspace, workspace_bytes, path, stream);
+}
+
+int moe_forward_padded_fp8(const void* x, const void* Wr, const void* br, const void* Wgu_q, const float* Wgu_s,
+                           const void* bgu, const void* Wd_q, const float* Wd_s, const void* bd, int64_t T,
+                           int32_t H, int32_t E, int32_t k, int32_t I, const int32_t* n_valid, void* y,
+                           int32_t* topk_ids_out, float* topk_w_out, int32_t* expert_counts_out, void* workspace,
+                           size_t workspace_bytes, int32_t path, void* stream) {
+  return forward_fp8("moe_forward_padded_fp8", x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, T, H, E, k, I,
+                     n_valid, y, topk_ids_out, topk_w_out, expert_counts_out, workspace, workspace_bytes, path,
+                     stream);
 }
 
 int moe_forward_fp8(const void* x, const void* Wr, const void* br, const void* Wgu_q, const float* Wgu_s,

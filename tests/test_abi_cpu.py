@@ -235,3 +235,20 @@ def test_probe_calls_validate(lib):
     assert lib.moe_probe_read(v, 24, 4, v, None) == INVALID and b"multiple of 16" in lib.moe_last_error()
     assert lib.moe_probe_read(ctypes.c_void_p(FAKE + 8), 32, 4, v, None) == INVALID
     assert lib.moe_probe_read(v, 32, 70000, v, None) == INVALID and b"workgroups" in lib.moe_last_error()
+
+
+@pytest.mark.parametrize("name", ["moe_forward_padded_mxfp4", "moe_forward_padded_fp8"])
+def test_padded_quantised_calls_validate(lib, name):
+    v = ctypes.c_void_p(FAKE)
+    p = [ctypes.c_void_p(FAKE)] * 10
+    fn = getattr(lib, name)
+
+    def call(n_valid=None, counts=None, path=0, T=4, ws=1 << 30, H=64, I=64):
+        return fn(*p[:9], T, H, 8, 2, I, n_valid, p[9], None, None, counts, v, ws, path, None)
+
+    assert call(n_valid=ctypes.c_void_p(FAKE + 2)) == INVALID and b"n_valid" in lib.moe_last_error()
+    assert call(counts=ctypes.c_void_p(FAKE + 1)) == INVALID and b"expert_counts_out" in lib.moe_last_error()
+    assert call(path=9) == INVALID and b"unknown path" in lib.moe_last_error()
+    assert call(ws=16) == WORKSPACE
+    assert call(H=40) == INVALID          # not a multiple of the format's block (32 for MXFP4, 16 for FP8)
+    assert call(T=0, n_valid=v, counts=v) == OK

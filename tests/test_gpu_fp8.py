@@ -240,3 +240,33 @@ def test_forward_configs(name):
                                            [0, cfg.T - 1]]))
     ref = orc.moe_forward_fp8(*arrays, k=k, tokens=tokens)["y"]
     assert_y_close(host_f64(y)[tokens], ref, f"y {name}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("nv", [0, 1, 37, 64, 80])
+def test_padded_forward(path, nv):
+    """Rows from n_valid on are padding: id -1, weight 0, y exactly 0, no
+    expert load; the valid rows and the loads match the oracle's FP8
+    forward of those rows alone (x and h rows are quantised per row, so the
+    padding cannot change a valid row's scales)."""
+    _need_gpu()
+    T, E, H, I, k = 64, 16, 256, 160, 4
+    cfg, arrays = _small(T, E, H, I, k, seed=13)
+    n_valid = torch.tensor([nv], dtype=torch.int32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts = torch.empty((E,), dtype=torch.int32, device="cuda")
+    y = binding.moe_forward_padded_fp8(*[_dev_any(a) for a in arrays], k=k, n_valid=n_valid, topk_ids=ids,
+                                       topk_w=w, expert_counts=counts, path=path)
+    n = min(nv, T)
+    yb, idh, wh = bf16_bits(y), ids.cpu().numpy(), w.cpu().numpy()
+    assert (yb[n:] == 0).all() and (idh[n:] == -1).all() and (wh[n:] == 0).all()
+    if n == 0:
+        assert (counts.cpu().numpy() == 0).all()
+        return
+    x, Wr, br = arrays[:3]
+    ids_ref, w_ref, lg = orc.route(x[:n], Wr, br, k)
+    assert (counts.cpu().numpy() == orc.expert_loads(ids_ref, E)).all()
+    assert_routing(idh[:n], wh[:n], ids_ref, w_ref, lg, k)
+    ref = orc.moe_forward_fp8(*arrays, k=k, tokens=np.arange(n))["y"]
+    assert_y_close(host_f64(y)[:n], ref, f"y n_valid={nv}")
