@@ -287,6 +287,29 @@ MOE_API int moe_forward_padded_fp8(const void* x, const void* Wr, const void* br
                                    int32_t* expert_counts_out, void* workspace, size_t workspace_bytes,
                                    int32_t path, void* stream);
 
+/* moe_forward_ep_mxfp4, moe_forward_ep_fp8 -- moe_forward_ep with MXFP4 or FP8
+ * expert weights: the rank's own experts [e_begin, e_begin + n_local) in the
+ * formats of moe_forward_mxfp4_ex and moe_forward_fp8_ex, indexed from 0
+ * (codes and scales of n_local experts; bgu_local, bd_local as in
+ * moe_forward_ep); workspace as moe_workspace_bytes or moe_workspace_bytes_fp8
+ * for the whole E.  y_partial (float32 [T][H]) and every other argument are as
+ * in moe_forward_ep: only local slots are computed, the others are skipped,
+ * and tokens with no local expert get 0. */
+MOE_API int moe_forward_ep_mxfp4(const void* x, const void* Wr, const void* br,
+                                 const void* Wgu_q_local, const void* Wgu_s_local, const void* bgu_local,
+                                 const void* Wd_q_local, const void* Wd_s_local, const void* bd_local,
+                                 int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                                 int32_t e_begin, int32_t n_local, float* y_partial,
+                                 int32_t* topk_ids_out, float* topk_w_out,
+                                 void* workspace, size_t workspace_bytes, int32_t path, void* stream);
+MOE_API int moe_forward_ep_fp8(const void* x, const void* Wr, const void* br,
+                               const void* Wgu_q_local, const float* Wgu_s_local, const void* bgu_local,
+                               const void* Wd_q_local, const float* Wd_s_local, const void* bd_local,
+                               int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                               int32_t e_begin, int32_t n_local, float* y_partial,
+                               int32_t* topk_ids_out, float* topk_w_out,
+                               void* workspace, size_t workspace_bytes, int32_t path, void* stream);
+
 /*
  * MXFP4 expert weights (W4A16) -- xserv "Phase 19: gpt-oss-20b MoE support",
  * section 5: the expert weights are 4-bit E2M1 values with one UE8M0

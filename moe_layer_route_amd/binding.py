@@ -28,7 +28,8 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace
            "moe_combine", "moe_quantize_mxfp4", "moe_forward_mxfp4", "moe_forward_mxfp4_ex", "moe_gate_up_mxfp4",
            "moe_down_mxfp4", "moe_quantize_fp8", "moe_quantize_rows_fp8", "moe_workspace_bytes_fp8",
            "moe_forward_fp8", "moe_forward_fp8_ex", "moe_gate_up_fp8", "moe_down_fp8", "moe_forward_padded",
-           "moe_probe_mfma_bf16", "moe_probe_read", "moe_forward_padded_mxfp4", "moe_forward_padded_fp8")
+           "moe_probe_mfma_bf16", "moe_probe_read", "moe_forward_padded_mxfp4", "moe_forward_padded_fp8",
+           "moe_forward_ep_mxfp4", "moe_forward_ep_fp8")
 
 
 class MoEError(RuntimeError):
@@ -71,6 +72,10 @@ _SIGS = {
                                  + [_vp, _sz, _i32, _vp]),
     "moe_forward_padded_fp8": (ctypes.c_int, [_vp] * 9 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 5
                                + [_vp, _sz, _i32, _vp]),
+    "moe_forward_ep_mxfp4": (ctypes.c_int, [_vp] * 9 + [_i64, _i32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 4
+                             + [_sz, _i32, _vp]),
+    "moe_forward_ep_fp8": (ctypes.c_int, [_vp] * 9 + [_i64, _i32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 4
+                           + [_sz, _i32, _vp]),
     "moe_probe_mfma_bf16": (ctypes.c_int, [_i32, _i32, _vp, _vp]),
     "moe_probe_read": (ctypes.c_int, [_vp, _sz, _i32, _vp, _vp]),
 }
@@ -530,6 +535,59 @@ def moe_forward_padded_fp8(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k: int 
                                           _stream(stream))
     _check(st, "moe_forward_padded_fp8")
     return y
+
+
+def moe_forward_ep_mxfp4(x, Wr, br, Wgu_q_local, Wgu_s_local, bgu_local, Wd_q_local, Wd_s_local, bd_local,
+                         e_begin: int, k: int = 4, y_partial=None, workspace=None, topk_ids=None, topk_w=None,
+                         path="auto", stream=None):
+    """moe_forward_ep with MXFP4 expert weights (the rank's n_local = Wgu_q_local.shape[0]
+    experts from e_begin); returns y_partial (float32 [T,H])."""
+    _dev(x, Wr, br, Wgu_q_local, Wgu_s_local, bgu_local, Wd_q_local, Wd_s_local, bd_local)
+    _b16(x, Wr, br, bgu_local, bd_local)
+    _u8(Wgu_q_local, Wgu_s_local, Wd_q_local, Wd_s_local)
+    T, H = x.shape
+    E = Wr.shape[0]
+    n_local = Wgu_q_local.shape[0]
+    I = Wd_q_local.shape[2] * 2
+    if y_partial is None:
+        y_partial = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(T, H, E, k, I, x.device)
+    _dev(y_partial, workspace, topk_ids, topk_w)
+    st = library().moe_forward_ep_mxfp4(_ptr(x), _ptr(Wr), _ptr(br), _ptr(Wgu_q_local), _ptr(Wgu_s_local),
+                                        _ptr(bgu_local), _ptr(Wd_q_local), _ptr(Wd_s_local), _ptr(bd_local), T, H,
+                                        E, k, I, e_begin, n_local, _ptr(y_partial), _ptr(topk_ids), _ptr(topk_w),
+                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        path_code(path), _stream(stream))
+    _check(st, "moe_forward_ep_mxfp4")
+    return y_partial
+
+
+def moe_forward_ep_fp8(x, Wr, br, Wgu_q_local, Wgu_s_local, bgu_local, Wd_q_local, Wd_s_local, bd_local,
+                       e_begin: int, k: int = 4, y_partial=None, workspace=None, topk_ids=None, topk_w=None,
+                       path="auto", stream=None):
+    """moe_forward_ep with FP8 W8A8 experts (the rank's n_local = Wgu_q_local.shape[0]
+    experts from e_begin); returns y_partial (float32 [T,H])."""
+    _dev(x, Wr, br, Wgu_q_local, Wgu_s_local, bgu_local, Wd_q_local, Wd_s_local, bd_local)
+    _b16(x, Wr, br, bgu_local, bd_local)
+    _u8(Wgu_q_local, Wd_q_local)
+    _f32(Wgu_s_local, Wd_s_local)
+    T, H = x.shape
+    E = Wr.shape[0]
+    n_local = Wgu_q_local.shape[0]
+    I = Wd_q_local.shape[2]
+    if y_partial is None:
+        y_partial = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace_fp8(T, H, E, k, I, x.device)
+    _dev(y_partial, workspace, topk_ids, topk_w)
+    st = library().moe_forward_ep_fp8(_ptr(x), _ptr(Wr), _ptr(br), _ptr(Wgu_q_local), _ptr(Wgu_s_local),
+                                      _ptr(bgu_local), _ptr(Wd_q_local), _ptr(Wd_s_local), _ptr(bd_local), T, H, E,
+                                      k, I, e_begin, n_local, _ptr(y_partial), _ptr(topk_ids), _ptr(topk_w),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      path_code(path), _stream(stream))
+    _check(st, "moe_forward_ep_fp8")
+    return y_partial
 
 
 # ---------------------------------------------------------------------------

@@ -425,10 +425,14 @@ static int run_down_mx(const char* fn, const void* h, const void* Wq, const void
 // on as padding, expert_counts_out (optional) receives the per-expert loads.
 static int forward_mxfp4(const char* fn, const void* x, const void* Wr, const void* br, const void* Wgu_q,
                          const void* Wgu_s, const void* bgu, const void* Wd_q, const void* Wd_s, const void* bd,
-                         int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, const int32_t* n_valid, void* y,
+                         int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, int32_t e_begin, int32_t n_local,
+                         const int32_t* n_valid, void* y, bool partial,
                          int32_t* topk_ids_out, float* topk_w_out, int32_t* expert_counts_out, void* workspace,
                          size_t workspace_bytes, int32_t path, void* stream) {
   if (int st = check_dims(fn, T, H, E, k, I)) return st;
+  if (n_local < 1 || e_begin < 0 || e_begin > E - n_local)
+    return fail(MOE_ERR_INVALID_ARG, "%s: local experts [%d, %d + %d) outside [0, E=%d)", fn, e_begin, e_begin,
+                n_local, E);
   if (int st = check_mx_dims(fn, H, I)) return st;
   CHECK_PTR(x, 16);
   CHECK_PTR(Wr, 16);
@@ -467,14 +471,16 @@ static int forward_mxfp4(const char* fn, const void* x, const void* Wr, const vo
   void* h = ws + L.h;
   float* o = reinterpret_cast<float*>(ws + L.o);
   hipStream_t s = (hipStream_t)stream;
+  // the expert path follows the whole layer's load per expert, T*k/E
+  path = choose_path(path, T, E, k);
 
   if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, ids, w, MOE_ROUTE_AUTO, s))) return st;
   if (n_valid)
     if (int st = hip_status(fn, moe::launch_mask_padding(ids, w, T, k, n_valid, s))) return st;
-  if (int st = hip_status(fn, moe::launch_permute(ids, T, E, k, cnt, off, rows, pos, s))) return st;
-  if (int st = run_gate_up_mx(fn, x, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, E, k, I, h, path, s)) return st;
-  if (int st = run_down_mx(fn, h, Wd_q, Wd_s, bd, cnt, off, T, H, E, k, I, o, path, s)) return st;
-  if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s))) return st;
+  if (int st = hip_status(fn, moe::launch_permute(ids, T, n_local, k, cnt, off, rows, pos, s, e_begin))) return st;
+  if (int st = run_gate_up_mx(fn, x, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, n_local, k, I, h, path, s)) return st;
+  if (int st = run_down_mx(fn, h, Wd_q, Wd_s, bd, cnt, off, T, H, n_local, k, I, o, path, s)) return st;
+  if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s, partial))) return st;
   return ok();
 }
 
@@ -482,8 +488,8 @@ int moe_forward_mxfp4_ex(const void* x, const void* Wr, const void* br, const vo
                          const void* bgu, const void* Wd_q, const void* Wd_s, const void* bd, int64_t T, int32_t H,
                          int32_t E, int32_t k, int32_t I, void* y, int32_t* topk_ids_out, float* topk_w_out,
                          void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
-  return forward_mxfp4("moe_forward_mxfp4", x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, T, H, E, k, I, nullptr, y,
-                       topk_ids_out, topk_w_out, nullptr, workspace, workspace_bytes, path, stream);
+  return forward_mxfp4("moe_forward_mxfp4", x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, T, H, E, k, I, 0, E,
+                       nullptr, y, false, topk_ids_out, topk_w_out, nullptr, workspace, workspace_bytes, path, stream);
 }
 
 int moe_forward_padded_mxfp4(const void* x, const void* Wr, const void* br, const void* Wgu_q, const void* Wgu_s,
@@ -492,8 +498,18 @@ int moe_forward_padded_mxfp4(const void* x, const void* Wr, const void* br, cons
                              int32_t* topk_ids_out, float* topk_w_out, int32_t* expert_counts_out, void* workspace,
                              size_t workspace_bytes, int32_t path, void* stream) {
   return forward_mxfp4("moe_forward_padded_mxfp4", x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, T, H, E, k, I,
-                       n_valid, y, topk_ids_out, topk_w_out, expert_counts_out, workspace, workspace_bytes, path,
-                       stream);
+                       0, E, n_valid, y, false, topk_ids_out, topk_w_out, expert_counts_out, workspace,
+                       workspace_bytes, path, stream);
+}
+
+int moe_forward_ep_mxfp4(const void* x, const void* Wr, const void* br, const void* Wgu_q_local,
+                         const void* Wgu_s_local, const void* bgu_local, const void* Wd_q_local,
+                         const void* Wd_s_local, const void* bd_local, int64_t T, int32_t H, int32_t E, int32_t k,
+                         int32_t I, int32_t e_begin, int32_t n_local, float* y_partial, int32_t* topk_ids_out,
+                         float* topk_w_out, void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
+  return forward_mxfp4("moe_forward_ep_mxfp4", x, Wr, br, Wgu_q_local, Wgu_s_local, bgu_local, Wd_q_local,
+                       Wd_s_local, bd_local, T, H, E, k, I, e_begin, n_local, nullptr, y_partial, true, topk_ids_out,
+                       topk_w_out, nullptr, workspace, workspace_bytes, path, stream);
 }
 
 int moe_forward_mxfp4(const void* x, const void* Wr, const void* br, const void* Wgu_q, const void* Wgu_s,
@@ -631,10 +647,14 @@ static int run_down_fp8(const char* fn, const void* hq, const float* sh, const v
 // as padding, expert_counts_out (optional) receives the per-expert loads.
 static int forward_fp8(const char* fn, const void* x, const void* Wr, const void* br, const void* Wgu_q,
                        const float* Wgu_s, const void* bgu, const void* Wd_q, const float* Wd_s, const void* bd,
-                       int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, const int32_t* n_valid, void* y,
+                       int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, int32_t e_begin, int32_t n_local,
+                         const int32_t* n_valid, void* y, bool partial,
                        int32_t* topk_ids_out, float* topk_w_out, int32_t* expert_counts_out, void* workspace,
                        size_t workspace_bytes, int32_t path, void* stream) {
   if (int st = check_dims(fn, T, H, E, k, I)) return st;
+  if (n_local < 1 || e_begin < 0 || e_begin > E - n_local)
+    return fail(MOE_ERR_INVALID_ARG, "%s: local experts [%d, %d + %d) outside [0, E=%d)", fn, e_begin, e_begin,
+                n_local, E);
   if (int st = check_fp8_dims(fn, H, I)) return st;
   CHECK_PTR(x, 16);
   CHECK_PTR(Wr, 16);
@@ -678,17 +698,19 @@ static int forward_fp8(const char* fn, const void* x, const void* Wr, const void
   void* hq = ws + F.hq;
   float* sh = reinterpret_cast<float*>(ws + F.sh);
   hipStream_t s = (hipStream_t)stream;
+  // the expert path follows the whole layer's load per expert, T*k/E
+  path = choose_path(path, T, E, k);
   const int64_t S = T * k;
 
   if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, ids, w, MOE_ROUTE_AUTO, s))) return st;
   if (n_valid)
     if (int st = hip_status(fn, moe::launch_mask_padding(ids, w, T, k, n_valid, s))) return st;
-  if (int st = hip_status(fn, moe::launch_permute(ids, T, E, k, cnt, off, rows, pos, s))) return st;
+  if (int st = hip_status(fn, moe::launch_permute(ids, T, n_local, k, cnt, off, rows, pos, s, e_begin))) return st;
   if (int st = hip_status(fn, moe::launch_fp8_quantize_rows(x, T, H, xq, sx, s))) return st;
-  if (int st = run_gate_up_fp8(fn, xq, sx, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, E, k, I, h, path, s)) return st;
+  if (int st = run_gate_up_fp8(fn, xq, sx, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, n_local, k, I, h, path, s)) return st;
   if (int st = hip_status(fn, moe::launch_fp8_quantize_rows(h, S, I, hq, sh, s))) return st;
-  if (int st = run_down_fp8(fn, hq, sh, Wd_q, Wd_s, bd, cnt, off, T, H, E, k, I, o, path, s)) return st;
-  if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s))) return st;
+  if (int st = run_down_fp8(fn, hq, sh, Wd_q, Wd_s, bd, cnt, off, T, H, n_local, k, I, o, path, s)) return st;
+  if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s, partial))) return st;
   return ok();
 }
 
@@ -696,8 +718,8 @@ int moe_forward_fp8_ex(const void* x, const void* Wr, const void* br, const void
                        const void* bgu, const void* Wd_q, const float* Wd_s, const void* bd, int64_t T, int32_t H,
                        int32_t E, int32_t k, int32_t I, void* y, int32_t* topk_ids_out, float* topk_w_out,
                        void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
-  return forward_fp8("moe_forward_fp8", x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, T, H, E, k, I, nullptr, y,
-                     topk_ids_out, topk_w_out, nullptr, workspace, workspace_bytes, path, stream);
+  return forward_fp8("moe_forward_fp8", x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, T, H, E, k, I, 0, E,
+                     nullptr, y, false, topk_ids_out, topk_w_out, nullptr, workspace, workspace_bytes, path, stream);
 }
 
 int moe_forward_padded_fp8(const void* x, const void* Wr, const void* br, const void* Wgu_q, const float* Wgu_s,
@@ -706,8 +728,18 @@ int moe_forward_padded_fp8(const void* x, const void* Wr, const void* br, const 
                            int32_t* topk_ids_out, float* topk_w_out, int32_t* expert_counts_out, void* workspace,
                            size_t workspace_bytes, int32_t path, void* stream) {
   return forward_fp8("moe_forward_padded_fp8", x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, T, H, E, k, I,
-                     n_valid, y, topk_ids_out, topk_w_out, expert_counts_out, workspace, workspace_bytes, path,
-                     stream);
+                     0, E, n_valid, y, false, topk_ids_out, topk_w_out, expert_counts_out, workspace,
+                     workspace_bytes, path, stream);
+}
+
+int moe_forward_ep_fp8(const void* x, const void* Wr, const void* br, const void* Wgu_q_local,
+                       const float* Wgu_s_local, const void* bgu_local, const void* Wd_q_local,
+                       const float* Wd_s_local, const void* bd_local, int64_t T, int32_t H, int32_t E, int32_t k,
+                       int32_t I, int32_t e_begin, int32_t n_local, float* y_partial, int32_t* topk_ids_out,
+                       float* topk_w_out, void* workspace, size_t workspace_bytes, int32_t path, void* stream) {
+  return forward_fp8("moe_forward_ep_fp8", x, Wr, br, Wgu_q_local, Wgu_s_local, bgu_local, Wd_q_local, Wd_s_local,
+                     bd_local, T, H, E, k, I, e_begin, n_local, nullptr, y_partial, true, topk_ids_out, topk_w_out,
+                     nullptr, workspace, workspace_bytes, path, stream);
 }
 
 int moe_forward_fp8(const void* x, const void* Wr, const void* br, const void* Wgu_q, const float* Wgu_s,

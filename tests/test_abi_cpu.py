@@ -252,3 +252,19 @@ def test_padded_quantised_calls_validate(lib, name):
     assert call(ws=16) == WORKSPACE
     assert call(H=40) == INVALID          # not a multiple of the format's block (32 for MXFP4, 16 for FP8)
     assert call(T=0, n_valid=v, counts=v) == OK
+
+
+@pytest.mark.parametrize("name", ["moe_forward_ep_mxfp4", "moe_forward_ep_fp8"])
+@pytest.mark.parametrize("e_begin,n_local", [(-1, 2), (0, 0), (7, 2), (0, 9)])
+def test_ep_quantised_calls_reject_bad_ranges(lib, name, e_begin, n_local):
+    p = [ctypes.c_void_p(FAKE)] * 10
+    st = getattr(lib, name)(*p[:9], 4, 64, 8, 2, 64, e_begin, n_local, p[9], None, None, p[0], 1 << 30, 0, None)
+    assert st == INVALID and b"local experts" in lib.moe_last_error()
+
+
+@pytest.mark.parametrize("name", ["moe_forward_ep_mxfp4", "moe_forward_ep_fp8"])
+def test_ep_quantised_calls_accept_valid_ranges(lib, name):
+    p = [ctypes.c_void_p(FAKE)] * 10
+    for lo, n in [(0, 8), (0, 1), (7, 1), (3, 4)]:
+        # T = 0: every check passes and nothing is enqueued
+        assert getattr(lib, name)(*p[:9], 0, 64, 8, 2, 64, lo, n, p[9], None, None, p[0], 1 << 30, 0, None) == OK

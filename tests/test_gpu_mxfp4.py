@@ -236,3 +236,31 @@ def test_padded_forward(path, nv):
     assert_routing(idh[:n], wh[:n], ids_ref, w_ref, lg, k)
     ref = orc.moe_forward_mxfp4(*arrays, k=k, tokens=np.arange(n))["y"]
     assert_y_close(host_f64(y)[:n], ref, f"y n_valid={nv}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("T,E,H,I,k,ranges", [
+    (64, 32, 2880, 2880, 4, [(0, 16), (16, 32)]),
+    (300, 8, 256, 160, 2, [(0, 1), (1, 5), (5, 8)]),     # uneven ranks
+])
+def test_expert_parallel_ranks_sum_to_y(T, E, H, I, k, ranges, path):
+    """Each rank's partial equals the oracle's forward over its expert range
+    (tokens with no local expert get exactly 0), and the partials sum to y."""
+    _need_gpu()
+    cfg, arrays = _small(T, E, H, I, k, seed=T + 3 * E)
+    x, Wr, br, gq, gs, bgu, dq, ds, bd = arrays
+    ref = orc.moe_forward_mxfp4(*arrays, k=k)
+    total = np.zeros((T, H))
+    for lo, hi in ranges:
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        local = [dev(np.ascontiguousarray(a[lo:hi])) for a in (gq, gs, bgu, dq, ds, bd)]
+        part = binding.moe_forward_ep_mxfp4(dev(x), dev(Wr), dev(br), *local, lo, k=k, topk_ids=ids, topk_w=w,
+                                        path=path).double().cpu().numpy()
+        assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], ref["logits"], k)
+        want = orc.moe_forward_mxfp4(*arrays, k=k, experts=(lo, hi))["y"]
+        assert_y_close(part, want, f"rank [{lo},{hi}) {path}")
+        none_here = ~((ref["ids"] >= lo) & (ref["ids"] < hi)).any(axis=1)
+        assert (part[none_here] == 0).all()
+        total += part
+    assert_y_close(total, ref["y"], f"sum of ranks {path}")
