@@ -264,9 +264,6 @@ def main(argv=None):
     mx = args.weights == "mxfp4"
     f8 = args.weights == "fp8"
     mx_arrays = f8_arrays = None
-    if (mx or f8) and args.ep > 1:
-        print("bench.py: --ep is measured with bf16 weights only", file=sys.stderr)
-        return 2
     if f8:
         gq, gs, bgu_f, dq, ds, bd_f = d.make_experts_fp8(cfg, seed=0)
         f8_arrays = (inp.x, inp.Wr, inp.br, gq, gs, bgu_f, dq, ds, bd_f)
@@ -275,9 +272,6 @@ def main(argv=None):
         del Wgu, Wd
         print("[bench] FP8 expert weights ready", file=sys.stderr, flush=True)
     if mx:
-        if args.ep > 1:
-            print("bench.py: --ep is measured with bf16 weights only", file=sys.stderr)
-            return 2
         gq, gs, bgu_m, dq, ds, bd_m = d.make_experts_mxfp4(cfg, seed=0)
         mx_arrays = (inp.x, inp.Wr, inp.br, gq, gs, bgu_m, dq, ds, bd_m)
         Wgu_q, Wgu_s, Wd_q, Wd_s = [torch.from_numpy(a).cuda() for a in (gq, gs, dq, ds)]
@@ -464,11 +458,15 @@ def main(argv=None):
             return 2
         nl = E // args.ep
         y_part = torch.empty((T, H), dtype=torch.float32, device="cuda")
-        local = [t[:nl] for t in (Wgu, bgu, Wd, bd)]
+        if mx or f8:
+            local = [t[:nl] for t in (Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd)]
+            ep_call = binding.moe_forward_ep_mxfp4 if mx else binding.moe_forward_ep_fp8
+        else:
+            local = [t[:nl] for t in (Wgu, bgu, Wd, bd)]
+            ep_call = binding.moe_forward_ep
 
         def ep_step():
-            binding.moe_forward_ep(x, Wr, br, *local, 0, k=k, y_partial=y_part, workspace=ws, path=args.path,
-                                   stream=stream)
+            ep_call(x, Wr, br, *local, 0, k=k, y_partial=y_part, workspace=ws, path=args.path, stream=stream)
 
         for _ in range(args.warmup):
             ep_step()

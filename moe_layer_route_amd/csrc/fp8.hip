@@ -112,12 +112,16 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 // ---------------------------------------------------------------------------
 constexpr int kRowWaves = 4;
 
+// R_live (device, optional): rows from *R_live on are left untouched (the
+// rows of h past the routed slots hold nothing and are never read).
 __global__ __launch_bounds__(kRowWaves * kWave) void fp8_rows_kernel(const bf16_t* __restrict__ a, int64_t R, int K,
+                                                                    const int32_t* __restrict__ R_live,
                                                                     uint8_t* __restrict__ codes,
                                                                     float* __restrict__ scales) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t r = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
   if (r >= R) return;                                    // wave-uniform, no barrier in this kernel
+  if (R_live && r >= (int64_t)*R_live) return;           // wave-uniform
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a + r * K);
   const int nch = K / 8;
   uint32_t m = 0;
@@ -713,12 +717,13 @@ hipError_t launch_gemv(const void* A, const float* a_scale, const void* Wq, cons
 
 }  // namespace
 
-hipError_t launch_fp8_quantize_rows(const void* a, int64_t R, int K, void* codes, float* scales, hipStream_t stream) {
+hipError_t launch_fp8_quantize_rows(const void* a, int64_t R, int K, void* codes, float* scales, hipStream_t stream,
+                                    const int32_t* R_live) {
   if (R == 0) return hipSuccess;
   const int64_t blocks = (R + kRowWaves - 1) / kRowWaves;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fp8_rows_kernel, dim3((unsigned)blocks), dim3(kRowWaves * kWave), 0, stream, (const bf16_t*)a, R,
-                     K, (uint8_t*)codes, scales);
+                     K, R_live, (uint8_t*)codes, scales);
   return hipGetLastError();
 }
 

@@ -57,7 +57,9 @@ hipError_t launch_gemm_mxfp4_down(const void* h, const void* Wq, const void* Ws,
 
 // FP8 W8A8 (OCP E4M3): weight codes [E][N][K] with one float32 scale per
 // expert; activation codes [R][K] with one scale per row (K % 16 == 0)
-hipError_t launch_fp8_quantize_rows(const void* a, int64_t R, int K, void* codes, float* scales, hipStream_t stream);
+// R_live (device int32, optional): only rows below *R_live are quantised
+hipError_t launch_fp8_quantize_rows(const void* a, int64_t R, int K, void* codes, float* scales, hipStream_t stream,
+                                    const int32_t* R_live = nullptr);
 hipError_t launch_fp8_quantize_weights(const void* W, int E, int K, int N, void* codes, float* scales,
                                        hipStream_t stream);
 hipError_t launch_gemm_fp8_gate_up(const void* xq, const float* sx, const void* Wq, const float* Ws, const void* bgu,

@@ -708,7 +708,9 @@ static int forward_fp8(const char* fn, const void* x, const void* Wr, const void
   if (int st = hip_status(fn, moe::launch_permute(ids, T, n_local, k, cnt, off, rows, pos, s, e_begin))) return st;
   if (int st = hip_status(fn, moe::launch_fp8_quantize_rows(x, T, H, xq, sx, s))) return st;
   if (int st = run_gate_up_fp8(fn, xq, sx, Wgu_q, Wgu_s, bgu, cnt, off, rows, T, H, n_local, k, I, h, path, s)) return st;
-  if (int st = hip_status(fn, moe::launch_fp8_quantize_rows(h, S, I, hq, sh, s))) return st;
+  // only the rows of h the permutation filled (off[n_local] of them; fewer
+  // than T*k with padding rows or on an expert-parallel rank)
+  if (int st = hip_status(fn, moe::launch_fp8_quantize_rows(h, S, I, hq, sh, s, off + n_local))) return st;
   if (int st = run_down_fp8(fn, hq, sh, Wd_q, Wd_s, bd, cnt, off, T, H, n_local, k, I, o, path, s)) return st;
   if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s, partial))) return st;
   return ok();
