@@ -227,7 +227,8 @@ def main(argv=None):
                     help="also time one expert-parallel rank's share of W ranks: experts [0, E/W), "
                          "all tokens routed (reported in ep_rank_share, not in value)")
     ap.add_argument("--n-valid", type=int, default=None,
-                    help="also time moe_forward_padded with this many valid rows (the rest padding), bf16 weights")
+                    help="also time the padded forward (moe_forward_padded and its MXFP4 / FP8 forms) with this many "
+                         "valid rows, the rest padding")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy, the reference kernel "
                          "that scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -426,13 +427,19 @@ def main(argv=None):
     step_s = ms_per_step * 1e-3
 
     padded = None
-    if args.n_valid is not None and not (mx or f8):
+    if args.n_valid is not None:
         nv_t = torch.tensor([args.n_valid], dtype=torch.int32, device="cuda")
         counts = torch.empty((E,), dtype=torch.int32, device="cuda")
 
         def pad_step():
-            binding.moe_forward_padded(x, Wr, br, Wgu, bgu, Wd, bd, k=k, n_valid=nv_t, y=y, workspace=ws,
-                                       topk_ids=ids, topk_w=w, expert_counts=counts, path=args.path, stream=stream)
+            if mx or f8:
+                (binding.moe_forward_padded_mxfp4 if mx else binding.moe_forward_padded_fp8)(
+                    x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k=k, n_valid=nv_t, y=y, workspace=ws,
+                    topk_ids=ids, topk_w=w, expert_counts=counts, path=args.path, stream=stream)
+            else:
+                binding.moe_forward_padded(x, Wr, br, Wgu, bgu, Wd, bd, k=k, n_valid=nv_t, y=y, workspace=ws,
+                                           topk_ids=ids, topk_w=w, expert_counts=counts, path=args.path,
+                                           stream=stream)
 
         for _ in range(args.warmup):
             pad_step()
