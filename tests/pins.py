@@ -693,9 +693,52 @@ def pin_fp8_forward_structure(orc):
     assert 1e-4 < rel < 0.15, rel          # E4M3 keeps 3 mantissa bits: a few percent
 
 
+# ---------------------------------------------------------------------------
+# Near-tie audit: hand-built logits whose gaps at each rank boundary are known
+# ---------------------------------------------------------------------------
+def pin_near_ties(orc):
+    """A token is a near tie when the float64 gap between the logits ranked
+    r and r+1 (r = 1 .. k, so the boundary between the last pick and the
+    first unpicked expert counts) is below rel * max(1, |higher logit|).
+    Each row below has one chosen gap at one boundary and gaps of 1 elsewhere;
+    the expected flags follow from the construction."""
+    rel = 1e-5
+    E, k = 8, 3
+    perm = np.array([5, 2, 7, 0, 3, 6, 1, 4])          # columns shuffled: the audit must sort
+    rows, want = [], []
+    for r in range(k + 2):                               # boundaries 1|2 .. k+2|k+3
+        for factor in (0.0, 0.5, 2.0):                   # exact tie, just below, just above the threshold
+            v = 20.0 - np.arange(E, dtype=np.float64)
+            thr = rel * v[r]                             # v[r] > 1: the scale is the logit itself
+            v[r + 1] = v[r] - factor * thr
+            v[r + 2:] = v[r + 1] - 1.0 - np.arange(E - r - 2)
+            rows.append(v[perm])
+            want.append(r < k and factor < 1.0)          # ranks r+1|r+2: audited up to k|k+1
+    # logits below 1 in magnitude: the threshold is rel itself
+    v = np.array([0.5, 0.5 - 0.7 * rel, -1.0, -2.0, -3.0, -4.0, -5.0, -6.0])
+    rows.append(v[perm]); want.append(True)
+    v = np.array([0.5, 0.5 - 1.5 * rel, -1.0, -2.0, -3.0, -4.0, -5.0, -6.0])
+    rows.append(v[perm]); want.append(False)
+    # negative logits: the scale is the magnitude, |-3| = 3
+    v = np.array([-3.0, -3.0 - 2.0 * rel, -5.0, -6.0, -7.0, -8.0, -9.0, -10.0])
+    rows.append(v[perm]); want.append(True)
+    v = np.array([-3.0, -3.0 - 4.0 * rel, -5.0, -6.0, -7.0, -8.0, -9.0, -10.0])
+    rows.append(v[perm]); want.append(False)
+    lg = np.stack(rows)
+    got = np.zeros(len(rows), dtype=bool)
+    got[orc.near_ties(lg, k, rel=rel)] = True
+    assert (got == np.array(want)).all(), (np.nonzero(got != np.array(want))[0], got, want)
+    # k = E - 1 audits every boundary; k = E cannot go past the last expert
+    v = 20.0 - np.arange(E, dtype=np.float64)
+    v[E - 1] = v[E - 2] - 0.5 * rel * v[E - 2]
+    assert orc.near_ties(v[None, perm], E - 1, rel=rel).tolist() == [0]
+    assert orc.near_ties(v[None, perm], E, rel=rel).tolist() == [0]
+    assert orc.near_ties(v[None, perm], E - 2, rel=rel).tolist() == []
+
+
 ALL_PINS = [pin_glu, pin_topk, pin_router, pin_permutation, pin_forward_bruteforce,
             pin_identical_experts, pin_structured_experts, pin_skip_semantics, pin_expert_ranges,
             pin_identity_glu_table, pin_e2m1_table, pin_ue8m0, pin_mxfp4_layout, pin_mxfp4_quantize_rne,
             pin_mxfp4_nearest, pin_mxfp4_forward, pin_e4m3_table, pin_e4m3_encode, pin_fp8_scales,
             pin_fp8_weight_layout, pin_fp8_gate_up_exact, pin_fp8_down_exact, pin_fp8_forward_structure,
-            pin_padded_batches]
+            pin_padded_batches, pin_near_ties]

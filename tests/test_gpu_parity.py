@@ -463,8 +463,10 @@ def _config_inputs(name):
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
 def test_forward_configs(name):
-    """Full-size forward; the oracle checks every token at c1/c2/c4 and a sample
-    (hot-expert tokens included) at c3/c5."""
+    """Full-size forward in the launch configuration the benchmark times; the
+    oracle computes every token, so every row of every (expert, M tile) of
+    the grouped-GEMM launches is compared, the last row of each expert
+    segment included."""
     _need_gpu()
     cfg, arrays = _config_inputs(name)
     k = cfg.k
@@ -473,16 +475,9 @@ def test_forward_configs(name):
     w = torch.empty((cfg.T, k), dtype=torch.float32, device="cuda")
     y = binding.moe_forward(*args, k=k, topk_ids=ids, topk_w=w)
     torch.cuda.synchronize()
-    ids_ref, w_ref, lg = orc.route(arrays[0], arrays[1], arrays[2], k)
-    assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, lg, k)
-    if cfg.T <= 256:
-        tokens = np.arange(cfg.T)
-    else:
-        rng = np.random.default_rng(0)
-        load = np.bincount(ids_ref.reshape(-1), minlength=cfg.E)
-        hot = np.nonzero((ids_ref == load.argmax()).any(axis=1))[0][:16]
-        tokens = np.unique(np.concatenate([rng.choice(cfg.T, 48, replace=False), hot, [0, cfg.T - 1]]))
-    ref = orc.moe_forward(*arrays, k=k, tokens=tokens)["y"]
-    assert_y_close(host_f64(y)[tokens], ref, f"y {name}")
+    print(f"[parity] bf16 {name}: GPU forward done, running the oracle over all {cfg.T} tokens", flush=True)
+    ref = orc.moe_forward(*arrays, k=k)
+    assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], ref["logits"], k)
+    assert_y_close(host_f64(y), ref["y"], f"y {name}")
     del args
     torch.cuda.empty_cache()

@@ -12,7 +12,8 @@ _real = {n: getattr(orc, n) for n in ("clamped_glu", "router_logits", "select_to
                                       "moe_forward", "widen", "mxfp4_quantize", "mxfp4_dequantize",
                                       "moe_forward_mxfp4", "ue8m0_decode", "e2m1_decode", "e4m3_encode",
                                       "fp8_scale", "fp8_quantize_rows", "fp8_quantize_weights", "bf16_round",
-                                      "moe_forward_fp8", "fp8_down", "expert_loads", "moe_forward_padded")}
+                                      "moe_forward_fp8", "fp8_down", "expert_loads", "moe_forward_padded",
+                                      "near_ties")}
 
 
 def _glu(gate_sel=0, up_sel=1, alpha=1.702, glim=(-np.inf, 7.0), ulim=(-7.0, 7.0), plus=1.0,
@@ -297,6 +298,18 @@ def _padded_variant(route_padding=False, off_by_one=False):
     return f
 
 
+
+def _near_ties(last_boundary=True, floor=True, signed=False, ascending=False):
+    def f(logits64, k, rel=1e-5):
+        s = np.sort(logits64, axis=1) if ascending else -np.sort(-logits64, axis=1)
+        kk = min(k + 1 if last_boundary else k, s.shape[1])
+        gaps = np.abs(s[:, :kk - 1] - s[:, 1:kk])
+        top = s[:, :kk - 1] if signed else np.abs(s[:, :kk - 1])
+        scale = np.maximum(1.0, top) if floor else top
+        return np.nonzero((gaps < rel * scale).any(axis=1))[0]
+    return f
+
+
 MUTANTS = {
     "loads_first_pick_only": ("expert_loads", _loads_first_pick_only),
     "padded_rows_routed": ("moe_forward_padded", _padded_variant(route_padding=True)),
@@ -350,6 +363,10 @@ MUTANTS = {
     "forward_expert_range_inclusive": ("moe_forward", _forward_range_inclusive),
     "forward_expert_range_ignored": ("moe_forward", _forward_range_ignored),
     "widen_drops_a_bit": ("widen", _widen_truncating),
+    "near_ties_drops_last_boundary": ("near_ties", _near_ties(last_boundary=False)),
+    "near_ties_no_floor_at_one": ("near_ties", _near_ties(floor=False)),
+    "near_ties_signed_scale": ("near_ties", _near_ties(signed=True)),
+    "near_ties_ascending": ("near_ties", _near_ties(ascending=True)),
 }
 
 
