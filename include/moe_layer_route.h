@@ -494,6 +494,18 @@ MOE_API int moe_probe_mfma_bf16(int32_t iters, int32_t workgroups, float* out, v
  * workgroups in [1, 65535]; bytes = 0 writes zeros. */
 MOE_API int moe_probe_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* out, void* stream);
 
+/* moe_probe_mfma_dot_bf16 -- out[m][n] = sum_k A[m][k] * B[n][k] formed as
+ * the MFMA router forms its logits (Phase 19 page, section 1 "MoE" row: the
+ * router is a Linear over the hidden state): v_mfma_f32_16x16x32_bf16 over K
+ * in steps of 32, in increasing K, into one float32 accumulator that starts
+ * at 0.  It exposes the instruction's own accumulation error, which the
+ * router's error bound has to cover.
+ *   A bf16 [M][K], B bf16 [16][K] (device, 16-byte aligned, row-major)
+ *   out float [M][16] (device, caller-owned)
+ * M a positive multiple of 16 (at most 16 * 65535), K a positive multiple of
+ * 32 (at most 2^20), A below 2 GiB; otherwise MOE_ERR_INVALID_ARG. */
+MOE_API int moe_probe_mfma_dot_bf16(const void* A, const void* B, int32_t M, int32_t K, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,7 +39,7 @@ hipError_t launch_gemm_down(const void* h, const void* Wd, const void* bd, const
                             const int32_t* off, int64_t T, int H, int E, int k, int I, float* o,
                             hipStream_t stream);
 
-// MXFP4 expert weights: codes [E][N][K/2], scales [E][N][K/32] (K % 32 == 0)
+// MXFP4 expert weights: codes [E][N][K/2], scales block-major [E][K/32][N] (K % 32 == 0)
 hipError_t launch_mxfp4_quantize(const void* W, int E, int K, int N, void* codes, void* scales, hipStream_t stream);
 hipError_t launch_mxfp4_gate_up(const void* x, const void* Wq, const void* Ws, const void* bgu, const int32_t* cnt,
                                 const int32_t* off, const int32_t* rows, int64_t T, int H, int E, int k, int I,
@@ -78,6 +78,7 @@ hipError_t launch_gemv_fp8_down(const void* hq, const float* sh, const void* Wq,
 // measurement probes (probe.hip)
 hipError_t launch_probe_mfma(int iters, int workgroups, float* out, hipStream_t stream);
 hipError_t launch_probe_read(const void* buf, size_t bytes, int workgroups, uint32_t* out, hipStream_t stream);
+hipError_t launch_probe_dot(const void* A, const void* B, int M, int K, float* out, hipStream_t stream);
 
 // slots with pos < 0 are left out; out_f32: y is float32 (partial sums), else bf16
 hipError_t launch_combine(const float* o, const int32_t* pos, const float* w, int64_t T, int H, int k,

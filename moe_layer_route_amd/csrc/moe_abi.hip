@@ -822,6 +822,21 @@ int moe_probe_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* 
   return ok();
 }
 
+int moe_probe_mfma_dot_bf16(const void* A, const void* B, int32_t M, int32_t K, float* out, void* stream) {
+  const char* fn = "moe_probe_mfma_dot_bf16";
+  if (M < 16 || M % 16 != 0 || M > 16 * 65535)
+    return fail(MOE_ERR_INVALID_ARG, "%s: M=%d is not a positive multiple of 16 (at most 16 * 65535)", fn, M);
+  if (K < 32 || K % 32 != 0 || K > (1 << 20))
+    return fail(MOE_ERR_INVALID_ARG, "%s: K=%d is not a positive multiple of 32 (at most 2^20)", fn, K);
+  if ((int64_t)M * K * 2 >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_INVALID_ARG, "%s: A of %d x %d exceeds 2 GiB", fn, M, K);
+  CHECK_PTR(A, 16);
+  CHECK_PTR(B, 16);
+  CHECK_PTR(out, 4);
+  if (int st = hip_status(fn, moe::launch_probe_dot(A, B, M, K, out, (hipStream_t)stream))) return st;
+  return ok();
+}
+
 int moe_combine(const float* o, const int32_t* pos, const float* topk_w, int64_t T, int32_t H, int32_t k,
                 void* y, void* stream) {
   const char* fn = "moe_combine";

@@ -14,6 +14,12 @@
 //   flight, XOR-folded and reduced to one word per wave.
 //   Each 16-byte piece is read exactly once, so the XOR of all outputs equals
 //   the XOR of the buffer's 32-bit words.
+// probe_dot_kernel: the bf16 dot products of rows of A with rows of B as the
+//   router forms them, v_mfma_f32_16x16x32_bf16 over K in steps of 32 into
+//   one float32 accumulator, so that the MFMA's own accumulation error can be
+//   measured against exact sums (bf16 x bf16 products are exact in float32;
+//   what the instruction does with a step's 32 products and the accumulator
+//   is not documented).  One wave per 16 rows of A.
 #include "device_common.h"
 #include "launch.h"
 
@@ -68,7 +74,27 @@ __global__ __launch_bounds__(kPbThreads) void probe_read_kernel(const u32x4_t* _
   if ((threadIdx.x & (kWave - 1)) == 0) out[blockIdx.x * kPbWaves + threadIdx.x / kWave] = x;
 }
 
+__global__ __launch_bounds__(kWave) void probe_dot_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
+                                                           int K, float* __restrict__ out) {
+  // lane l: A row 16 b + l%16 and B row l%16, K chunk 8 (l/16) of every step
+  const int lane = threadIdx.x;
+  const int c = lane & 15, g = lane >> 4;
+  const bf16_t* a = A + ((size_t)blockIdx.x * 16 + c) * K + 8 * g;
+  const bf16_t* b = B + (size_t)c * K + 8 * g;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < K; k0 += 32) acc = mfma16x16x32(ld16(a + k0), ld16(b + k0), acc);
+  // accumulator layout: lane l, element v = A row 4 (l/16) + v, B row l%16
+#pragma unroll
+  for (int v = 0; v < 4; ++v) out[((size_t)blockIdx.x * 16 + 4 * g + v) * 16 + c] = acc[v];
+}
+
 }  // namespace
+
+hipError_t launch_probe_dot(const void* A, const void* B, int M, int K, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(probe_dot_kernel, dim3((unsigned)(M / 16)), dim3(kWave), 0, stream, (const bf16_t*)A,
+                     (const bf16_t*)B, K, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_probe_mfma(int iters, int workgroups, float* out, hipStream_t stream) {
   hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)workgroups), dim3(kPbThreads), 0, stream, iters, out);

@@ -235,6 +235,15 @@ def test_probe_calls_validate(lib):
     assert lib.moe_probe_read(v, 24, 4, v, None) == INVALID and b"multiple of 16" in lib.moe_last_error()
     assert lib.moe_probe_read(ctypes.c_void_p(FAKE + 8), 32, 4, v, None) == INVALID
     assert lib.moe_probe_read(v, 32, 70000, v, None) == INVALID and b"workgroups" in lib.moe_last_error()
+    dot = lib.moe_probe_mfma_dot_bf16
+    assert dot(v, v, 24, 64, v, None) == INVALID and b"M=24" in lib.moe_last_error()
+    assert dot(v, v, 0, 64, v, None) == INVALID
+    assert dot(v, v, 16, 48, v, None) == INVALID and b"K=48" in lib.moe_last_error()
+    assert dot(v, v, 16 * 65536, 64, v, None) == INVALID
+    assert dot(v, v, 16 * 40000, 1 << 16, v, None) == INVALID and b"2 GiB" in lib.moe_last_error()
+    assert dot(ctypes.c_void_p(FAKE + 4), v, 16, 64, v, None) == INVALID
+    assert dot(v, None, 16, 64, v, None) == INVALID
+    assert dot(v, v, 16, 64, None, None) == INVALID and b"out" in lib.moe_last_error()
 
 
 @pytest.mark.parametrize("name", ["moe_forward_padded_mxfp4", "moe_forward_padded_fp8"])
