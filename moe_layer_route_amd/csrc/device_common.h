@@ -87,6 +87,18 @@ __device__ __forceinline__ float clamped_glu(float gate, float up) {
   return (u + 1.0f) * (g * s);
 }
 
+// Orders one wave's LDS accesses where its lanes exchange data through LDS:
+// the accesses before it are done, as every lane of the wave sees them,
+// before the accesses after it.  The LDS carries out one wave's operations
+// in issue order, so this only keeps the compiler from moving a lane's
+// accesses across it (whose addresses it could prove distinct); it adds no
+// instruction.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // streaming (read-once) 16-byte load
 __device__ __forceinline__ u32x4_t ldg16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));

@@ -606,11 +606,13 @@ void gemv_fp8_kernel(
       }
     };
     auto step = [&](const F8W& dw, const F8A<MG>& da) {
-      // stage through the slab (a wave's LDS accesses complete in order, so
-      // the reads see this step's writes; the next step's writes follow the
-      // reads' data arriving in registers)
+      // stage through the slab: other lanes read what a lane writes, so the
+      // writes are fenced from the previous step's reads and from this
+      // step's reads
+      wave_lds_fence();
 #pragma unroll
       for (int i = 0; i < 8; ++i) my_slab[w_dst[i]] = dw.w[i];
+      wave_lds_fence();
       u32x4_t bw[kF8NJ][2];
 #pragma unroll
       for (int j = 0; j < kF8NJ; ++j) {

@@ -248,11 +248,13 @@ void gemv_mxfp4_kernel(
     // double step d: half step u = 0 uses a0 (and loads a1 with half step
     // 2d+1), u = 1 uses a1 (and loads a0 with 2d+2)
     auto step = [&](int d, const MxSlot& sl) {
-      // stage the codes through the slab (a wave's LDS accesses complete in
-      // order: the reads see this step's writes, the next step's writes come
-      // after these reads)
+      // stage the codes through the slab: other lanes read what a lane
+      // writes, so the writes are fenced from the previous step's reads and
+      // from this step's reads
+      wave_lds_fence();
 #pragma unroll
       for (int i = 0; i < 8; ++i) my_slab[w_dst[i]] = sl.w[i];
+      wave_lds_fence();
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const MxA<MG>& ac = u == 0 ? a0 : a1;
