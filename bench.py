@@ -1,20 +1,30 @@
 """Benchmark of the MI355X MoE block forward (one JSON line on stdout).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5] [--decode-workload c2]
+                    [--no-cpu-baseline]
 
 A step is one whole moe_forward (router + top-k + permutation + gate_up/GLU +
 down + combine) over one batch of seeded synthetic input already resident in
-HBM.  The default workload is the gpt-oss-20b MoE block at decode batch
-T = 64 (H = I = 2880, E = 32, top-4, bf16 weights N(0, 0.02), biases N(0, 0.01),
-router bias 0, x scaled so ~5% of gate/up pre-activations hit the clamp,
-seed 0).  `value` is tokens per second of the whole job.
+HBM.  The headline workload is the largest single-GPU one: the
+gpt-oss-120b-shaped MoE block at prefill, T = 16384 tokens, H = I = 2880,
+E = 128 experts, top-4, bf16 weights N(0, 0.02), biases N(0, 0.01), x scaled
+so ~5% of gate/up pre-activations hit the clamp, router bias drawn Zipf(1.1)
+over the experts (skewed loads, the hottest expert > 10x the mean), seed 0.
+`value` is tokens per second of the whole job, from K steps run back to back
+(warm caches) between two HIP events on the launch stream; `ms_per_step` is
+that time / K.  The same workload's per-step p50 with the caches flushed
+before every step is reported beside it (`cold_latency_us`).
 
-Two extra objects:
+Extra objects:
   roofline      the dominant kernel (the gate_up expert kernel, two thirds of
-                the bytes): algorithmic bytes per launch / its mean launch time,
-                timed with HIP events on the stream it runs on;
-  cpu_baseline  the float64 oracle timed on the host cores over a bounded
-                sample of the same workload (a baseline, not the target).
+                the flops and bytes): algorithmic flops (prefill) or bytes
+                (decode) per launch / its mean launch time, timed with HIP
+                events on the stream it runs on;
+  decode        the same measurement, compactly, for the decode batch
+                (gpt-oss-20b block, T = 64, E = 32): tokens/s, the gate_up
+                kernel's HBM roofline and the whole layer's;
+  cpu_baseline  the float64 oracle timed on the host cores over the whole
+                headline batch (a baseline, not the target).
 Context fields: per-step latency percentiles with warm and with cold caches
 (a 512 MiB buffer written before each cold step, outside its events), the
 time per step of a HIP graph replaying one captured step, and what a plain
@@ -212,54 +222,33 @@ def _achievable(torch):
             "probe_mfma_bf16_TFLOPs": 1024 * 4 * 4096 * 8 * 32768 / t_mfma / 1e12, "probe_mfma_check": mfma_ok}
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
-    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
-    ap.add_argument("--weights", default="bf16", choices=["bf16", "mxfp4", "fp8"],
-                    help="expert weight format: bf16 (moe_forward), MXFP4 W4A16 (moe_forward_mxfp4) or FP8 "
-                         "W8A8 (moe_forward_fp8)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--ep", type=int, default=1,
-                    help="also time one expert-parallel rank's share of W ranks: experts [0, E/W), "
-                         "all tokens routed (reported in ep_rank_share, not in value)")
-    ap.add_argument("--n-valid", type=int, default=None,
-                    help="also time the padded forward (moe_forward_padded and its MXFP4 / FP8 forms) with this many "
-                         "valid rows, the rest padding")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="first run a plain 1 GiB device-to-device copy, the reference kernel "
-                         "that scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
-    args = ap.parse_args(argv)
+def _timed_steps(torch, step, stream, steps):
+    """Mean time of `steps` back-to-back steps between two events on `stream` (ms)."""
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        return 2
 
+def measure(args, name, headline=True):
+    """Time one workload: the whole step, its latency percentiles (warm, cold,
+    graph replay) and the dominant kernel.  Returns (record, inputs, format
+    arrays for the oracle)."""
     import numpy as np
     import torch
     from moe_layer_route_amd import binding, datagen as d
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    cfg = d.CONFIGS[args.workload]
+    cfg = d.CONFIGS[name]
     inp = d.make_inputs(cfg, seed=0)
     print(f"[bench] inputs ready: {cfg.name} T={cfg.T} E={cfg.E}", file=sys.stderr, flush=True)
 
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-
-    if args.copy_probe:
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        print("[bench] copy probe: 1 GiB read + 1 GiB written", file=sys.stderr, flush=True)
 
     x, Wr, br, Wgu, bgu, Wd, bd = [dev(a) for a in inp.arrays()]
     mx = args.weights == "mxfp4"
@@ -301,16 +290,8 @@ def main(argv=None):
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    ms_per_step = _timed_steps(torch, step, stream, args.steps)
+    print(f"[bench] {name}: timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     # Per-step latency: every step between its own pair of events, warm caches.
     lat = _per_step_us(torch, step, stream, args.steps)
@@ -329,17 +310,9 @@ def main(argv=None):
     with torch.cuda.graph(graph):
         step(torch.cuda.current_stream())
     graph.replay()
-    torch.cuda.synchronize()
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    g0.record(stream)
-    for _ in range(args.steps):
-        graph.replay()
-    g1.record(stream)
-    torch.cuda.synchronize()
-    graph_ms = g0.elapsed_time(g1) / args.steps
+    graph_ms = _timed_steps(torch, graph.replay, stream, args.steps)
     del graph
-    print(f"[bench] per-step p50 {lat['p50']:.1f} us, cold p50 {cold['p50']:.1f} us, "
+    print(f"[bench] {name}: per-step p50 {lat['p50']:.1f} us, cold p50 {cold['p50']:.1f} us, "
           f"graph replay {graph_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     # Dominant kernel: the same pipeline through the stage calls, with events
@@ -397,27 +370,16 @@ def main(argv=None):
                "moe_layer_route_amd/csrc/fp8.hip" if f8 else f"moe_layer_route_amd/csrc/{path}.hip")
     gu_stem = "fp8_gemv" if f8 and path == "gemv" else "fp8_gemm" if f8 else None
     traffic = _traffic(gu_file, cfg.name, stem=gu_stem)
-    if f8 and path == "gemv":
-        roofline = {"bound": "hbm", "kernel": "gemv_fp8_kernel<gate_up>",
-                    "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    elif f8:
-        roofline = {"bound": "mfma", "kernel": "gemm_fp8_kernel<gate_up>",
-                    "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12, "peak": FP8_PEAK_TFLOPS,
-                    "unit": "TFLOP/s"}
-    elif mx and path == "gemv":
-        roofline = {"bound": "hbm", "kernel": "gemv_mxfp4_kernel<gate_up>",
-                    "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    elif mx:
-        roofline = {"bound": "mfma", "kernel": "gemm_mxfp4_kernel<gate_up>",
-                    "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s"}
-    elif path == "gemv":
-        roofline = {"bound": "hbm", "kernel": "gemv_expert_kernel<gate_up>",
-                    "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    kernel = {("fp8", "gemv"): "gemv_fp8_kernel<gate_up>", ("fp8", "gemm"): "gemm_fp8_kernel<gate_up>",
+              ("mxfp4", "gemv"): "gemv_mxfp4_kernel<gate_up>", ("mxfp4", "gemm"): "gemm_mxfp4_kernel<gate_up>",
+              ("bf16", "gemv"): "gemv_expert_kernel<gate_up>",
+              ("bf16", "gemm"): "gemm_expert_kernel<gate_up>"}[(args.weights, path)]
+    if path == "gemv":
+        roofline = {"bound": "hbm", "kernel": kernel, "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
-        roofline = {"bound": "mfma", "kernel": "gemm_expert_kernel<gate_up>",
-                    "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s"}
+        roofline = {"bound": "mfma", "kernel": kernel, "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12,
+                    "peak": FP8_PEAK_TFLOPS if f8 else BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roofline.update(frac=roofline["achieved"] / roofline["peak"], traffic=traffic,
                     alg_bytes_per_launch=gu_bytes, alg_flops_per_launch=gu_flops, launch_us=gate_up_ms * 1e3)
     layer_bytes = (_alg_bytes_layer_mxfp4(cfg, D) if mx else _alg_bytes_layer_fp8(cfg, D) if f8
@@ -425,6 +387,23 @@ def main(argv=None):
     mfma_peak = FP8_PEAK_TFLOPS if f8 else BF16_PEAK_TFLOPS
     layer_flops = _alg_flops_layer(cfg)
     step_s = ms_per_step * 1e-3
+    rec = {
+        "workload": f"{cfg.name}: {cfg.description}",
+        "T": T, "H": H, "I": I, "E": E, "k": k, "seed": 0, "path": path, "live_experts": D,
+        "weights": args.weights,
+        "ms_per_step": ms_per_step,
+        "tokens_per_s": T / step_s,
+        "roofline": roofline,
+        "layer": {"alg_bytes": layer_bytes, "alg_flops": layer_flops,
+                  "hbm_GBs": layer_bytes / step_s / 1e9, "hbm_frac": layer_bytes / step_s / 1e9 / HBM_PEAK_GBS,
+                  "tflops": layer_flops / step_s / 1e12,
+                  "mfma_frac": layer_flops / step_s / 1e12 / mfma_peak},
+        "latency_us": lat,
+        "cold_latency_us": cold,
+        "graph_ms_per_step": graph_ms,
+    }
+    if not headline:
+        return rec, None, None
 
     padded = None
     if args.n_valid is not None:
@@ -443,26 +422,16 @@ def main(argv=None):
 
         for _ in range(args.warmup):
             pad_step()
-        torch.cuda.synchronize()
-        p0 = torch.cuda.Event(enable_timing=True)
-        p1 = torch.cuda.Event(enable_timing=True)
-        p0.record(stream)
-        for _ in range(args.steps):
-            pad_step()
-        p1.record(stream)
-        torch.cuda.synchronize()
-        pad_ms = p0.elapsed_time(p1) / args.steps
+        pad_ms = _timed_steps(torch, pad_step, stream, args.steps)
         nv = min(max(args.n_valid, 0), T)
         padded = {"n_valid": nv, "ms_per_step": pad_ms, "valid_tokens_per_s": nv / (pad_ms * 1e-3),
                   "live_experts": int((counts > 0).sum().item()), "max_expert_load": int(counts.max().item())}
         print(f"[bench] padded batch ({nv} of {T} rows valid): {pad_ms * 1e3:.1f} us/step", file=sys.stderr,
               flush=True)
+    rec["padded"] = padded
 
     ep_share = None
     if args.ep > 1:
-        if E % args.ep:
-            print(f"bench.py: E={E} is not divisible by --ep {args.ep}", file=sys.stderr)
-            return 2
         nl = E // args.ep
         y_part = torch.empty((T, H), dtype=torch.float32, device="cuda")
         if mx or f8:
@@ -477,52 +446,104 @@ def main(argv=None):
 
         for _ in range(args.warmup):
             ep_step()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            ep_step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ep_ms = e0.elapsed_time(e1) / args.steps
+        ep_ms = _timed_steps(torch, ep_step, stream, args.steps)
         local_slots = int(((ids >= 0) & (ids < nl)).sum().item())
         ep_share = {"ranks": args.ep, "local_experts": nl, "local_slots": local_slots, "ms_per_step": ep_ms,
                     "tokens_per_s_per_rank": T / (ep_ms * 1e-3)}
         print(f"[bench] expert-parallel rank share ({nl} of {E} experts): {ep_ms * 1e3:.1f} us/step",
               file=sys.stderr, flush=True)
+    rec["ep_rank_share"] = ep_share
+    return rec, inp, (mx_arrays, f8_arrays)
 
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"],
+                    help="headline workload (default c5, the largest single-GPU configuration)")
+    ap.add_argument("--decode-workload", default="c2", choices=["none", "c1", "c2", "c3", "c4", "c5"],
+                    help="second workload reported in the `decode` key (default c2, the decode batch)")
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
+    ap.add_argument("--weights", default="bf16", choices=["bf16", "mxfp4", "fp8"],
+                    help="expert weight format: bf16 (moe_forward), MXFP4 W4A16 (moe_forward_mxfp4) or FP8 "
+                         "W8A8 (moe_forward_fp8)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-achievable", action="store_true", help="skip the copy / probe / hipBLASLt context")
+    ap.add_argument("--ep", type=int, default=1,
+                    help="also time one expert-parallel rank's share of W ranks: experts [0, E/W), "
+                         "all tokens routed (reported in ep_rank_share, not in value)")
+    ap.add_argument("--n-valid", type=int, default=None,
+                    help="also time the padded forward (moe_forward_padded and its MXFP4 / FP8 forms) with this many "
+                         "valid rows, the rest padding")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy, the reference kernel "
+                         "that scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    from moe_layer_route_amd import datagen as d
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.ep > 1 and d.CONFIGS[args.workload].E % args.ep:
+        print(f"bench.py: E={d.CONFIGS[args.workload].E} is not divisible by --ep {args.ep}", file=sys.stderr)
+        return 2
+
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("[bench] copy probe: 1 GiB read + 1 GiB written", file=sys.stderr, flush=True)
+
+    rec, inp, (mx_arrays, f8_arrays) = measure(args, args.workload, headline=True)
+    torch.cuda.empty_cache()
+    decode = None
+    if args.decode_workload not in ("none", args.workload):
+        decode, _, _ = measure(args, args.decode_workload, headline=False)
+        torch.cuda.empty_cache()
+
+    cfg = inp.cfg
     out = {
         "metric": METRIC,
-        "value": T / step_s,
+        "value": rec["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if f8 else "bf16",
+        "dtype": "fp8" if args.weights == "fp8" else "bf16",
         "data": "synthetic (seeded normal bf16 inputs of the gpt-oss MoE block shapes; random-init weights)",
-        "config": {"workload": f"{cfg.name}: {cfg.description}", "T": T, "H": H, "I": I, "E": E, "k": k,
-                   "seed": 0, "path": path, "live_experts": D, "weights": args.weights},
-        "roofline": roofline,
-        "layer": {"alg_bytes": layer_bytes, "alg_flops": layer_flops,
-                  "hbm_GBs": layer_bytes / step_s / 1e9, "hbm_frac": layer_bytes / step_s / 1e9 / HBM_PEAK_GBS,
-                  "tflops": layer_flops / step_s / 1e12,
-                  "mfma_frac": layer_flops / step_s / 1e12 / mfma_peak},
-        "latency_us": lat,
-        "cold_latency_us": cold,
-        "graph_ms_per_step": graph_ms,
-        "achievable": _achievable(torch),
-        "ep_rank_share": ep_share,
-        "padded": padded,
+        "timing": "value and ms_per_step: K steps back to back (warm caches) between two HIP events on the "
+                  "launch stream; cold_latency_us: per-step percentiles with a 512 MiB write before each step",
+        "config": {k: rec[k] for k in ("workload", "T", "H", "I", "E", "k", "seed", "path", "live_experts",
+                                        "weights")},
+        "roofline": rec["roofline"],
+        "layer": rec["layer"],
+        "latency_us": rec["latency_us"],
+        "cold_latency_us": rec["cold_latency_us"],
+        "graph_ms_per_step": rec["graph_ms_per_step"],
+        "decode": decode,
+        "achievable": None if args.no_achievable else _achievable(torch),
+        "ep_rank_share": rec["ep_rank_share"],
+        "padded": rec["padded"],
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp, k, mx_arrays=mx_arrays, f8_arrays=f8_arrays)
+        out["cpu_baseline"] = cpu_baseline(inp, cfg.k, mx_arrays=mx_arrays, f8_arrays=f8_arrays)
     print(json.dumps(out), flush=True)
     return 0
 
