@@ -159,6 +159,27 @@ MOE_API int moe_forward_ex(const void* x, const void* Wr, const void* br,
                    void* workspace, size_t workspace_bytes, int32_t path, void* stream);
 
 /*
+ * moe_forward_noalloc -- moe_forward without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, meaning
+ * and result bits as moe_forward (same kernels, path chosen as MOE_PATH_AUTO);
+ * the caller still owns x, the weights, y and the optional id/weight outputs.
+ * The intermediates live in a 64 MiB array of the library's own, one per GPU,
+ * held until the process ends: about T*k*(2I + 4H + 16) bytes are needed
+ * (T*k <= 3880 at H = I = 2880, i.e. T <= 970 at k = 4), and larger sizes
+ * return MOE_ERR_INVALID_ARG without enqueuing anything.  Nothing is
+ * allocated and nothing needs to start at zero.  Every call on a GPU shares
+ * that GPU's array and finds the last call's contents in it: calls that
+ * overlap on one GPU (different streams, or host threads) race and must be
+ * serialised by the caller.  The first call on a device looks the array's
+ * address up on that device (the device current on the calling thread).
+ */
+MOE_API int moe_forward_noalloc(const void* x, const void* Wr, const void* br,
+                                const void* Wgu, const void* bgu, const void* Wd, const void* bd,
+                                int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                                void* y, int32_t* topk_ids_out, float* topk_w_out, void* stream);
+
+/*
  * moe_forward_ep -- one expert-parallel rank's share of the layer: experts
  * are split across ranks by contiguous ranges, every rank routes all T tokens
  * over all E experts, keeps only the (token, slot) pairs whose expert it holds

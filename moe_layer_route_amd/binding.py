@@ -29,7 +29,8 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace
            "moe_down_mxfp4", "moe_quantize_fp8", "moe_quantize_rows_fp8", "moe_workspace_bytes_fp8",
            "moe_forward_fp8", "moe_forward_fp8_ex", "moe_gate_up_fp8", "moe_down_fp8", "moe_forward_padded",
            "moe_probe_mfma_bf16", "moe_probe_read", "moe_forward_padded_mxfp4", "moe_forward_padded_fp8",
-           "moe_forward_ep_mxfp4", "moe_forward_ep_fp8", "moe_probe_mfma_dot_bf16")
+           "moe_forward_ep_mxfp4", "moe_forward_ep_fp8", "moe_probe_mfma_dot_bf16",
+           "moe_forward_noalloc")
 
 
 class MoEError(RuntimeError):
@@ -79,6 +80,7 @@ _SIGS = {
     "moe_probe_mfma_bf16": (ctypes.c_int, [_i32, _i32, _vp, _vp]),
     "moe_probe_read": (ctypes.c_int, [_vp, _sz, _i32, _vp, _vp]),
     "moe_probe_mfma_dot_bf16": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    "moe_forward_noalloc": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32] + [_vp] * 4),
 }
 
 
@@ -281,6 +283,24 @@ def moe_forward(x, Wr, br, Wgu, bgu, Wd, bd, k: int = 4, y=None, workspace=None,
                                   workspace.numel() * workspace.element_size(), path_code(path),
                                   _stream(stream))
     _check(st, "moe_forward")
+    return y
+
+
+def moe_forward_noalloc(x, Wr, br, Wgu, bgu, Wd, bd, k: int = 4, y=None, topk_ids=None, topk_w=None, stream=None):
+    """moe_forward on the library's own scratch array (no workspace argument;
+    the call itself allocates nothing).  For T*k*(2I + 4H + 16) bytes up to
+    64 MiB; calls that overlap on one GPU race.  Returns y (bf16 [T,H])."""
+    T, H, E = _route_args(x, Wr, br, k, topk_ids, topk_w)
+    _bf16_experts(Wgu, bgu, Wd, bd, E, H)
+    I = Wd.shape[1]
+    _req(y, "y", (T, H), torch.bfloat16)
+    _dev(x, Wr, br, Wgu, bgu, Wd, bd)
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _dev(y, topk_ids, topk_w)
+    _check(library().moe_forward_noalloc(_ptr(x), _ptr(Wr), _ptr(br), _ptr(Wgu), _ptr(bgu), _ptr(Wd), _ptr(bd),
+                                         T, H, E, k, I, _ptr(y), _ptr(topk_ids), _ptr(topk_w), _stream(stream)),
+           "moe_forward_noalloc")
     return y
 
 

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe_layer_route.h"
 #include "launch.h"
 
@@ -112,6 +114,100 @@ int run_down(const char* fn, const void* h, const void* Wd, const void* bd, cons
   return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
 }
 
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free forward: a file-scope device array (each GPU
+// the library runs on holds its own copy until the process ends).  In host
+// code its name is only a stand-in for the symbol, so the device address is
+// looked up once per device with that device current and kept; kernels and
+// every host call get that address, never the name.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+int scratch_on_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: device %d is beyond the %d the library tracks", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MOE_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// Host-side checks of the whole forward's arguments (nothing is enqueued).
+int check_forward(const char* fn, const void* x, const void* Wr, const void* br, const void* Wgu, const void* bgu,
+                  const void* Wd, const void* bd, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                  const void* y, const int32_t* topk_ids_out, const float* topk_w_out, int32_t path) {
+  if (int st = check_dims(fn, T, H, E, k, I)) return st;
+  CHECK_PTR(x, 16);
+  CHECK_PTR(Wr, 16);
+  CHECK_PTR(br, 2);
+  CHECK_PTR(Wgu, 16);
+  CHECK_PTR(bgu, 4);
+  CHECK_PTR(Wd, 16);
+  CHECK_PTR(bd, 4);
+  CHECK_PTR(y, 16);
+  if (topk_ids_out && !aligned(topk_ids_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_ids_out is not 4-byte aligned", fn);
+  if (topk_w_out && !aligned(topk_w_out, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_w_out is not 4-byte aligned", fn);
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+  return MOE_OK;
+}
+
+// The whole forward on a caller-provided (or the library's own) workspace.
+int forward_impl(const char* fn, const void* x, const void* Wr, const void* br, const void* Wgu, const void* bgu,
+                 const void* Wd, const void* bd, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I, void* y,
+                 int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes, int32_t path,
+                 void* stream) {
+  if (int st = check_forward(fn, x, Wr, br, Wgu, bgu, Wd, bd, T, H, E, k, I, y, topk_ids_out, topk_w_out, path))
+    return st;
+  if (T == 0) return ok();
+  const Layout L = layout(T, H, E, k, I);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, L.total);
+  if (!aligned(workspace, 256))
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.cnt);
+  int32_t* off = reinterpret_cast<int32_t*>(ws + L.off);
+  int32_t* rows = reinterpret_cast<int32_t*>(ws + L.rows);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+  void* h = ws + L.h;
+  float* o = reinterpret_cast<float*>(ws + L.o);
+  hipStream_t s = (hipStream_t)stream;
+
+  if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, ids, w, MOE_ROUTE_AUTO, s))) return st;
+  if (int st = hip_status(fn, moe::launch_permute(ids, T, E, k, cnt, off, rows, pos, s))) return st;
+  if (int st = run_gate_up(fn, x, Wgu, bgu, cnt, off, rows, T, H, E, k, I, h, path, s)) return st;
+  if (int st = run_down(fn, h, Wd, bd, cnt, off, T, H, E, k, I, o, path, s)) return st;
+  if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s))) return st;
+  return ok();
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -167,47 +263,28 @@ int moe_forward_ex(const void* x, const void* Wr, const void* br, const void* Wg
                    const void* Wd, const void* bd, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
                    void* y, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
                    size_t workspace_bytes, int32_t path, void* stream) {
-  const char* fn = "moe_forward";
-  if (int st = check_dims(fn, T, H, E, k, I)) return st;
-  CHECK_PTR(x, 16);
-  CHECK_PTR(Wr, 16);
-  CHECK_PTR(br, 2);
-  CHECK_PTR(Wgu, 16);
-  CHECK_PTR(bgu, 4);
-  CHECK_PTR(Wd, 16);
-  CHECK_PTR(bd, 4);
-  CHECK_PTR(y, 16);
-  if (topk_ids_out && !aligned(topk_ids_out, 4))
-    return fail(MOE_ERR_INVALID_ARG, "%s: topk_ids_out is not 4-byte aligned", fn);
-  if (topk_w_out && !aligned(topk_w_out, 4))
-    return fail(MOE_ERR_INVALID_ARG, "%s: topk_w_out is not 4-byte aligned", fn);
-  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM)
-    return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+  return forward_impl("moe_forward", x, Wr, br, Wgu, bgu, Wd, bd, T, H, E, k, I, y, topk_ids_out, topk_w_out,
+                      workspace, workspace_bytes, path, stream);
+}
+
+int moe_forward_noalloc(const void* x, const void* Wr, const void* br, const void* Wgu, const void* bgu,
+                        const void* Wd, const void* bd, int64_t T, int32_t H, int32_t E, int32_t k, int32_t I,
+                        void* y, int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  const char* fn = "moe_forward_noalloc";
+  if (int st = check_forward(fn, x, Wr, br, Wgu, bgu, Wd, bd, T, H, E, k, I, y, topk_ids_out, topk_w_out,
+                             MOE_PATH_AUTO))
+    return st;
   if (T == 0) return ok();
-  const Layout L = layout(T, H, E, k, I);
-  if (workspace == nullptr || workspace_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
-                workspace ? workspace_bytes : (size_t)0, L.total);
-  if (!aligned(workspace, 256))
-    return fail(MOE_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
-
-  char* ws = static_cast<char*>(workspace);
-  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
-  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
-  int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.cnt);
-  int32_t* off = reinterpret_cast<int32_t*>(ws + L.off);
-  int32_t* rows = reinterpret_cast<int32_t*>(ws + L.rows);
-  int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
-  void* h = ws + L.h;
-  float* o = reinterpret_cast<float*>(ws + L.o);
-  hipStream_t s = (hipStream_t)stream;
-
-  if (int st = hip_status(fn, moe::launch_route(x, Wr, br, T, H, E, k, ids, w, MOE_ROUTE_AUTO, s))) return st;
-  if (int st = hip_status(fn, moe::launch_permute(ids, T, E, k, cnt, off, rows, pos, s))) return st;
-  if (int st = run_gate_up(fn, x, Wgu, bgu, cnt, off, rows, T, H, E, k, I, h, path, s)) return st;
-  if (int st = run_down(fn, h, Wd, bd, cnt, off, T, H, E, k, I, o, path, s)) return st;
-  if (int st = hip_status(fn, moe::launch_combine(o, pos, w, T, H, k, y, s))) return st;
-  return ok();
+  const size_t need = layout(T, H, E, k, I).total;
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_INVALID_ARG,
+                "%s: T=%lld, H=%d, E=%d, k=%d, I=%d need %zu bytes of scratch; the library's array holds %zu "
+                "(about T*k*(2I + 4H + 16) bytes are needed): use moe_forward with a workspace",
+                fn, (long long)T, H, E, k, I, need, kScratchBytes);
+  void* ws = nullptr;
+  if (int st = scratch_on_current_device(fn, &ws)) return st;
+  return forward_impl(fn, x, Wr, br, Wgu, bgu, Wd, bd, T, H, E, k, I, y, topk_ids_out, topk_w_out, ws,
+                      kScratchBytes, MOE_PATH_AUTO, stream);
 }
 
 int moe_forward_ep(const void* x, const void* Wr, const void* br, const void* Wgu_local, const void* bgu_local,

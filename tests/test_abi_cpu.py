@@ -226,6 +226,21 @@ def test_padded_calls_validate(lib):
     assert call(T=0, n_valid=v, counts=v) == OK
 
 
+def test_noalloc_forward_validates_before_touching_the_gpu(lib):
+    v = ctypes.c_void_p(FAKE)
+    p = [v] * 7
+    fn = lib.moe_forward_noalloc
+    assert fn(*p, 0, 2880, 32, 4, 2880, v, None, None, None) == OK
+    assert fn(None, *p[1:], 4, 64, 8, 2, 64, v, None, None, None) == INVALID and b"x is NULL" in lib.moe_last_error()
+    assert fn(*p, 4, 64, 8, 2, 64, None, None, None, None) == INVALID and b"y is NULL" in lib.moe_last_error()
+    assert fn(*p, 4, 64, 8, 9, 64, v, None, None, None) == INVALID and b"k=9" in lib.moe_last_error()
+    assert fn(*p, 4, 64, 8, 2, 64, v, ctypes.c_void_p(FAKE + 2), None, None) == INVALID
+    # beyond the 64 MiB array: rejected with the size it would need
+    assert fn(*p, 4096, 2880, 32, 4, 2880, v, None, None, None) == INVALID
+    msg = lib.moe_last_error()
+    assert b"moe_forward_noalloc" in msg and b"scratch" in msg and str(64 << 20).encode() in msg
+
+
 def test_probe_calls_validate(lib):
     v = ctypes.c_void_p(FAKE)
     assert lib.moe_probe_mfma_bf16(0, 4, v, None) == INVALID and b"iters" in lib.moe_last_error()
