@@ -743,15 +743,21 @@ hipError_t launch_fp8_quantize_weights(const void* W, int E, int K, int N, void*
   return hipGetLastError();
 }
 
+// The LDS-staged 256 x 256 kernel (fp8_gemm.hip) where K % 16 == 0, this
+// kernel otherwise.
 hipError_t launch_gemm_fp8_gate_up(const void* xq, const float* sx, const void* Wq, const float* Ws, const void* bgu,
                                    const int32_t* cnt, const int32_t* off, const int32_t* rows, int64_t T, int H,
                                    int E, int k, int I, void* h, hipStream_t stream) {
+  const hipError_t st = launch_gemm_fp8_lds_gate_up(xq, sx, Wq, Ws, bgu, cnt, off, rows, T, H, E, k, I, h, stream);
+  if (st != hipErrorNotSupported) return st;
   return launch_gemm<true>(xq, sx, Wq, Ws, bgu, cnt, off, rows, T, H, 2 * I, E, k, h, stream);
 }
 
 hipError_t launch_gemm_fp8_down(const void* hq, const float* sh, const void* Wq, const float* Ws, const void* bd,
                                 const int32_t* cnt, const int32_t* off, int64_t T, int H, int E, int k, int I,
                                 float* o, hipStream_t stream) {
+  const hipError_t st = launch_gemm_fp8_lds_down(hq, sh, Wq, Ws, bd, cnt, off, T, H, E, k, I, o, stream);
+  if (st != hipErrorNotSupported) return st;
   return launch_gemm<false>(hq, sh, Wq, Ws, bd, cnt, off, nullptr, T, I, H, E, k, o, stream);
 }
 

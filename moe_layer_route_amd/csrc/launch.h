@@ -39,6 +39,15 @@ hipError_t launch_gemm_down(const void* h, const void* Wd, const void* bd, const
                             const int32_t* off, int64_t T, int H, int E, int k, int I, float* o,
                             hipStream_t stream);
 
+// FP8 tiled GEMM staged through LDS by direct loads (fp8_gemm.hip); returns
+// hipErrorNotSupported for K % 16 != 0 (or 2I % 64 != 0 for gate_up)
+hipError_t launch_gemm_fp8_lds_gate_up(const void* xq, const float* sx, const void* Wq, const float* Ws,
+                                       const void* bgu, const int32_t* cnt, const int32_t* off, const int32_t* rows,
+                                       int64_t T, int H, int E, int k, int I, void* h, hipStream_t stream);
+hipError_t launch_gemm_fp8_lds_down(const void* hq, const float* sh, const void* Wq, const float* Ws, const void* bd,
+                                    const int32_t* cnt, const int32_t* off, int64_t T, int H, int E, int k, int I,
+                                    float* o, hipStream_t stream);
+
 // MXFP4 expert weights: codes [E][N][K/2], scales block-major [E][K/32][N] (K % 32 == 0)
 hipError_t launch_mxfp4_quantize(const void* W, int E, int K, int N, void* codes, void* scales, hipStream_t stream);
 hipError_t launch_mxfp4_gate_up(const void* x, const void* Wq, const void* Ws, const void* bgu, const int32_t* cnt,
