@@ -99,6 +99,41 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Raw buffer descriptor words (base, byte range, stride 0) for the direct-to-LDS
+// loads below; an offset at or past `bytes` reads 0 and touches no memory.
+__device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// 16 bytes per lane from the buffer at voff + soff into LDS at lds + 16 * lane.
+// Issued as assembly: the compiler would otherwise wait for every such load
+// before any later LDS read.  M0 holds the LDS address (one wait state after
+// writing it); the loads count in vmcnt and the waits are explicit.
+__device__ __forceinline__ void dma16(u32x4_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(soff), "s"(lds)
+               : "memory");
+}
+// The same with 4 bytes per lane, into LDS at lds + 4 * lane.
+__device__ __forceinline__ void dma4(u32x4_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(soff), "s"(lds)
+               : "memory");
+}
+
 // streaming (read-once) 16-byte load
 __device__ __forceinline__ u32x4_t ldg16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));

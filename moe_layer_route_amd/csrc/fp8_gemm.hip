@@ -64,31 +64,6 @@ constexpr int kQgMBlock = 8;                            // M tiles per block of 
 constexpr int kXcds = 8;
 constexpr uint32_t kQgOOR = 0x80000000u;               // beyond every descriptor's range
 
-__device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)base;
-  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
-}
-
-// 16 bytes per lane from the buffer at voff + soff into LDS at lds + 16 * lane.
-// Issued as assembly: the compiler would otherwise wait for every such load
-// before any later LDS read.  M0 holds the LDS address (one wait state after
-// writing it); the loads count in vmcnt and the waits are explicit.
-__device__ __forceinline__ void dma16(u32x4_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :
-               : "v"(voff), "s"(rs), "s"(soff), "s"(lds)
-               : "memory");
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
-  return v;
-}
-
 __device__ __forceinline__ f32x16_t mfma_fp8_32(const u32x4_t (&a)[2], const u32x4_t (&b)[2], f32x16_t c) {
   const i32x8_t av = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
                       (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};

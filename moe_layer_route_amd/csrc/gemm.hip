@@ -59,15 +59,6 @@ struct GemmSmem {
   u32x4_t a[kGmLdsBufs][kGmBM / 16][kWave];   // 3 x 8 fragments x 1 KB
 };
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
-  return v;
-}
-
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Raw buffer descriptor over [base, base + bytes): loads whose vector offset

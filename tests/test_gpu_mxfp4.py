@@ -108,6 +108,27 @@ def test_forward_sweep(T, E, H, I, k, path):
     assert_y_close(host_f64(y), ref["y"], f"y T{T} E{E} H{H} I{I} k{k}")
 
 
+@pytest.mark.parametrize("T,E,H,I,k,bias,min_max_rows", [
+    (40, 16, 2880, 2880, 4, "zipf", 17),   # skewed decode batch: an expert with more than one 16-row chunk
+    (3, 2, 96, 32, 2, "normal", 1),        # two experts; down N = 96: one and a half 64-column slices
+    (12, 8, 2880, 64, 4, "zipf", 1),       # gate_up N = 128: two slices; down K = 64
+    (24, 64, 2848, 2880, 4, "normal", 1),  # K = 2848: the last 256-value step holds one block of eight
+])
+def test_decode_batch_shapes(T, E, H, I, k, bias, min_max_rows):
+    """Decode batches (T*k <= 10 E, the weight-streaming kernel's one-chunk regime) against the oracle, ids
+    and y: an expert with more than 16 rows, very few experts, a single column quad, K cut inside a line."""
+    _need_gpu()
+    assert T * k <= 10 * E
+    cfg, arrays = _small(T, E, H, I, k, seed=T + 7 * E, router_bias=bias)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y = _run(arrays, k, topk_ids=ids, topk_w=w, path="gemv")
+    ref = orc.moe_forward_mxfp4(*arrays, k=k)
+    assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], ref["logits"], k)
+    assert np.bincount(ref["ids"].ravel(), minlength=E).max() >= min_max_rows
+    assert_y_close(host_f64(y), ref["y"], f"y T{T} E{E} H{H} I{I} k{k}")
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_stage_intermediates(path):
     """gate_up and down alone against the oracle's h and o, matched through pos."""
