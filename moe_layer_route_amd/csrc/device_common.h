@@ -109,6 +109,56 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
+// Tile order of the grouped expert GEMMs, one launch for all experts.  Expert e
+// has ceil(cnt[e] / bm) M tiles x n_tiles N tiles.  Tiles go expert by expert;
+// within an expert, blocks of at most mblock M tiles take each N tile in turn
+// (the block's M tiles share that N tile's weight slab, and its N tiles share
+// the block's token rows).  Block b runs on XCD b % 8, and consecutive tiles go
+// to one XCD, whose L2 then serves both reuses.  Every lane of the calling wave
+// gets the same expert, first row and N tile; false for a block past the last
+// tile (the grid is an upper bound).  Experts 4 lane .. 4 lane + 3: E <= 256.
+__device__ __forceinline__ bool grouped_gemm_tile(const int32_t* __restrict__ cnt, int E, int bm, int n_tiles,
+                                                  int mblock, int lane, int& e, int& m0, int& nt) {
+  constexpr int kXcdCount = 8;
+  int mt[4], tc[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ee = lane * 4 + i;
+    mt[i] = ee < E ? (cnt[ee] + bm - 1) / bm : 0;
+    tc[i] = mt[i] * n_tiles;
+    sum += tc[i];
+  }
+  const int incl = wave_incl_scan(sum, lane);
+  const int R = __shfl(incl, kWave - 1, kWave);
+  const int Q = (R + kXcdCount - 1) / kXcdCount;
+  const int xi = (int)blockIdx.x / kXcdCount;
+  const int L = (int)(blockIdx.x % kXcdCount) * Q + xi;
+  int fe = -1, fm = 0, fn = 0;
+  if (xi < Q && L < R) {
+    int start = incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (L >= start && L < start + tc[i]) {
+        const int t = L - start;
+        const int mb = t / (mblock * n_tiles);
+        const int rows_b = min(mblock, mt[i] - mb * mblock);
+        const int t2 = t - mb * mblock * n_tiles;
+        fe = lane * 4 + i;
+        fm = (mb * mblock + t2 % rows_b) * bm;
+        fn = t2 / rows_b;
+      }
+      start += tc[i];
+    }
+  }
+  const uint64_t found = __ballot(fe >= 0);
+  if (found == 0) return false;
+  const int src = __ffsll((unsigned long long)found) - 1;
+  e = __builtin_amdgcn_readfirstlane(__shfl(fe, src, kWave));
+  m0 = __builtin_amdgcn_readfirstlane(__shfl(fm, src, kWave));
+  nt = __builtin_amdgcn_readfirstlane(__shfl(fn, src, kWave));
+  return true;
+}
+
 // Raw buffer descriptor words (base, byte range, stride 0) for the direct-to-LDS
 // loads below; an offset at or past `bytes` reads 0 and touches no memory.
 __device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {

@@ -92,45 +92,11 @@ __global__ __launch_bounds__(kQgThreads, 1) void gemm_fp8_lds_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- workgroup -> (expert, M tile, N tile); every wave finds the same ----
-  int fe = -1, fm = 0, fn = 0;
-  {
-    int mt[4], tc[4], sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane * 4 + i;
-      mt[i] = e < E ? (cnt[e] + kQgBM - 1) / kQgBM : 0;
-      tc[i] = mt[i] * n_tiles;
-      sum += tc[i];
-    }
-    const int incl = wave_incl_scan(sum, lane);
-    const int R = __shfl(incl, kWave - 1, kWave);
-    const int Q = (R + kXcds - 1) / kXcds;
-    const int xi = blockIdx.x / kXcds;
-    const int L = (blockIdx.x % kXcds) * Q + xi;
-    if (xi < Q && L < R) {
-      int start = incl - sum;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (L >= start && L < start + tc[i]) {
-          const int t = L - start;
-          const int mb = t / (kQgMBlock * n_tiles);
-          const int rows_b = min(kQgMBlock, mt[i] - mb * kQgMBlock);
-          const int t2 = t - mb * kQgMBlock * n_tiles;
-          fe = lane * 4 + i;
-          fm = (mb * kQgMBlock + t2 % rows_b) * kQgBM;
-          fn = t2 / rows_b;
-        }
-        start += tc[i];
-      }
-    }
-  }
-  const uint64_t found = __ballot(fe >= 0);
-  if (found == 0) return;                                    // workgroup-uniform
-  const int src = __ffsll((unsigned long long)found) - 1;
-  const int e = __builtin_amdgcn_readfirstlane(__shfl(fe, src, kWave));
-  const int m0 = __builtin_amdgcn_readfirstlane(__shfl(fm, src, kWave));
-  const int n0 = __builtin_amdgcn_readfirstlane(__shfl(fn, src, kWave)) * kQgBN;
+  // ---- workgroup -> (expert, M tile, N tile): the grouped tile order, every
+  // wave finds the same ----
+  int e, m0, nt;
+  if (!grouped_gemm_tile(cnt, E, kQgBM, n_tiles, kQgMBlock, lane, e, m0, nt)) return;   // workgroup-uniform
+  const int n0 = nt * kQgBN;
   const int M = cnt[e];
   const int row0 = off[e];
   const int ns = (K + kQgBK - 1) / kQgBK;

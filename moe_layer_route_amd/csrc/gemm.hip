@@ -8,11 +8,11 @@
 //
 // One launch covers every expert.  The grid is sized from host-known T, k, E
 // only: (number of N tiles) x (an upper bound on the M tiles of all experts,
-// ceil(T*k / BM) + E).  Each workgroup looks up which expert and which rows its
-// M-tile slot holds from cnt[] (prefix sum of ceil(cnt[e] / BM)); surplus
-// slots exit before any load or barrier.  Linear block ids are remapped so
-// that consecutive tiles (the M tiles of one expert on one N tile, which share
-// the weight slab) run on the same XCD, whose L2 serves the reuse.
+// ceil(T*k / BM) + E).  Each workgroup finds its (expert, M tile, N tile) from
+// cnt[] (prefix sum of ceil(cnt[e] / BM) x N tiles); surplus blocks exit before
+// any load or barrier.  Tiles go expert by expert, in blocks of at most eight M
+// tiles that take each N tile's weight slab in turn, and consecutive tiles run
+// on one XCD, whose L2 serves both reuses.
 //
 // Tile: 128 rows x 512 columns, K steps of 32, four waves (one per SIMD) side
 // by side along N.  Each wave owns 128 rows x 128 columns = 8 x 8 tiles of
@@ -53,6 +53,7 @@ constexpr int kGmBN = kGmWaves * kGmWN;       // 512
 constexpr int kGmBK = 32;
 constexpr int kGmLdsBufs = 3;
 constexpr int kXcds = 8;
+constexpr int kGmMBlock = 8;   // M tiles per block of the tile order
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // a voffset no descriptor here reaches
 
 struct GemmSmem {
@@ -77,47 +78,18 @@ __global__ __launch_bounds__(kGmThreads, 1) void gemm_expert_kernel(
     const bf16_t* __restrict__ bias,   // [E][N]
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ off,
     const int32_t* __restrict__ rows,  // gate_up: permuted slot ids
-    int K, int N, int E, int kslots, int a_rows, int n_tiles, int m_slots, void* __restrict__ out) {
+    int K, int N, int E, int kslots, int a_rows, int n_tiles, void* __restrict__ out) {
   __shared__ __align__(16) GemmSmem sm;
-  __shared__ int s_tile[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   // wave-uniform, stated so: it selects LDS fragments and weight columns
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
-  // ---- block -> (N tile, M-tile slot), consecutive slots on one XCD ----
-  const int per_xcd = gridDim.x / kXcds;
-  const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (L >= n_tiles * m_slots) return;                       // block-uniform
-  const int nt = L / m_slots;
-  const int ms = L - nt * m_slots;
-
-  // ---- M-tile slot -> (expert, first row) ----
-  if (wave == 0) {
-    if (lane == 0) s_tile[0] = -1;
-    int tc[4];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane * 4 + i;
-      tc[i] = e < E ? (cnt[e] + kGmBM - 1) / kGmBM : 0;
-      sum += tc[i];
-    }
-    int start = wave_incl_scan(sum, lane) - sum;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (ms >= start && ms < start + tc[i]) {
-        s_tile[0] = lane * 4 + i;
-        s_tile[1] = (ms - start) * kGmBM;
-      }
-      start += tc[i];
-    }
-  }
-  __syncthreads();
-  const int e = s_tile[0];
-  if (e < 0) return;                                         // block-uniform
-  const int m0 = s_tile[1];
+  // ---- block -> (expert, M tile, N tile): the grouped tile order, every wave
+  // finds the same ----
+  int e, m0, nt;
+  if (!grouped_gemm_tile(cnt, E, kGmBM, n_tiles, kGmMBlock, lane, e, m0, nt)) return;   // block-uniform
   const int M = cnt[e];
   const int row0 = off[e];
   const int n0 = nt * kGmBN;
@@ -326,7 +298,7 @@ hipError_t launch(const void* A, const void* W, const void* bias, const int32_t*
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_expert_kernel<GATE_UP>), dim3((unsigned)grid), dim3(kGmThreads), 0, stream,
                      (const bf16_t*)A, (const bf16_t*)W, (const bf16_t*)bias, cnt, off, rows, K, N, E, k,
-                     (int)a_rows, n_tiles, (int)m_slots, out);
+                     (int)a_rows, n_tiles, out);
   return hipGetLastError();
 }
 

@@ -7,8 +7,8 @@
 // section 5 (one batched launch for all experts) and section 4 (early exits
 // only when the whole workgroup leaves together; masked tails).
 //
-// The tiling, the tile lookup, the token-row LDS ring and the epilogue are
-// those of the bf16 grouped GEMM (gemm.hip): 128 x 512 tiles, four waves (one
+// The tiling, the token-row LDS ring and the epilogue are those of the bf16
+// grouped GEMM (gemm.hip): 128 x 512 tiles, four waves (one
 // per SIMD) of 128 x 128, 8 x 8 tiles of v_mfma_f32_16x16x32_bf16 with the
 // accumulators in the AGPRs.  What changes is the weight operand:
 //   the codes are K-contiguous ([E][N][K/2]), so lane (g = lane/16,
@@ -94,6 +94,11 @@ __global__ __launch_bounds__(kMgThreads, 1) void gemm_mxfp4_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
   // ---- block -> (N tile, M-tile slot), consecutive slots on one XCD ----
+  // For one N tile every M tile of every expert in turn (an expert's M tiles
+  // share the N tile's weight slab in the XCD's L2).  The blocked expert order
+  // of the bf16 and FP8 kernels, whose concurrent tiles also share token rows,
+  // runs this kernel about 1.5x slower: here the token rows are half of each
+  // step's loads.
   const int per_xcd = gridDim.x / kXcds;
   const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (L >= n_tiles * m_slots) return;                       // block-uniform
