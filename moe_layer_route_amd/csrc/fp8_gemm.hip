@@ -37,8 +37,8 @@
 //   are issued into the other buffer (its reads ended before that barrier);
 //   each wave waits for its own loads at the end of the stage and the barrier
 //   makes all of them visible.
-// Tile order: expert by expert; within an expert in blocks of at most 8 M
-// tiles, each N tile's weight slab taken by the block's M tiles in turn,
+// Tile order: expert by expert; within an expert, each N tile's weight slab
+// taken by all the expert's M tiles in turn (256-row tiles: a few per expert),
 // consecutive tiles on one XCD (workgroup b runs on XCD b % 8).  Workgroups
 // past the tile count exit before any load or barrier.
 #include "device_common.h"
@@ -60,7 +60,7 @@ constexpr int kQgOpBytes = kQgBM * kQgRowBytes;         // 32 KB: one operand of
 constexpr int kQgA = 0;                                 // A of buffer b at b * 32 KB
 constexpr int kQgB = 2 * kQgOpBytes;                    // B of buffer b at 64 KB + b * 32 KB
 constexpr int kQgLds = 4 * kQgOpBytes;                  // 128 KB
-constexpr int kQgMBlock = 8;                            // M tiles per block of the tile order
+constexpr int kQgMBlock = 1024;   // M tiles per block of the tile order: all of an expert's
 constexpr int kXcds = 8;
 constexpr uint32_t kQgOOR = 0x80000000u;               // beyond every descriptor's range
 

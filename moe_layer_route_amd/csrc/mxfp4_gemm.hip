@@ -7,8 +7,8 @@
 // section 5 (one batched launch for all experts) and section 4 (early exits
 // only when the whole workgroup leaves together; masked tails).
 //
-// The tiling, the token-row LDS ring and the epilogue are those of the bf16
-// grouped GEMM (gemm.hip): 128 x 512 tiles, four waves (one
+// The tiling, the tile order, the token-row LDS ring and the epilogue are
+// those of the bf16 grouped GEMM (gemm.hip): 128 x 512 tiles, four waves (one
 // per SIMD) of 128 x 128, 8 x 8 tiles of v_mfma_f32_16x16x32_bf16 with the
 // accumulators in the AGPRs.  What changes is the weight operand:
 //   the codes are K-contiguous ([E][N][K/2]), so lane (g = lane/16,
@@ -43,6 +43,7 @@ constexpr int kMgWN = 128;                    // columns per wave
 constexpr int kMgBN = kMgWaves * kMgWN;       // 512
 constexpr int kMgLdsBufs = 3;
 constexpr int kXcds = 8;
+constexpr int kMgMBlock = 8;   // M tiles per block of the tile order
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // a voffset no descriptor here reaches
 
 struct MgSmem {
@@ -85,51 +86,32 @@ __global__ __launch_bounds__(kMgThreads, 1) void gemm_mxfp4_kernel(
     const bf16_t* __restrict__ bias,   // [E][N]
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ off,
     const int32_t* __restrict__ rows,  // gate_up: permuted slot ids
-    int K, int N, int E, int kslots, int a_rows, int n_tiles, int m_slots, void* __restrict__ out) {
+    int K, int N, int E, int kslots, int a_rows, int n_tiles, void* __restrict__ out) {
   __shared__ __align__(16) MgSmem sm;
-  __shared__ int s_tile[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
-  // ---- block -> (N tile, M-tile slot), consecutive slots on one XCD ----
-  // For one N tile every M tile of every expert in turn (an expert's M tiles
-  // share the N tile's weight slab in the XCD's L2).  The blocked expert order
-  // of the bf16 and FP8 kernels, whose concurrent tiles also share token rows,
-  // runs this kernel about 1.5x slower: here the token rows are half of each
-  // step's loads.
-  const int per_xcd = gridDim.x / kXcds;
-  const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (L >= n_tiles * m_slots) return;                       // block-uniform
-  const int nt = L / m_slots;
-  const int ms = L - nt * m_slots;
-
-  // ---- M-tile slot -> (expert, first row) ----
+  // ---- block -> (expert, M tile, N tile): the grouped tile order.  Wave 0
+  // finds it and hands it over through LDS (the lookup's registers, live in
+  // every wave, would push this kernel's accumulator-bound allocation into
+  // spills) ----
+  __shared__ int s_tile[3];
   if (wave == 0) {
-    if (lane == 0) s_tile[0] = -1;
-    int tc[4];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane * 4 + i;
-      tc[i] = e < E ? (cnt[e] + kMgBM - 1) / kMgBM : 0;
-      sum += tc[i];
-    }
-    int start = wave_incl_scan(sum, lane) - sum;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (ms >= start && ms < start + tc[i]) {
-        s_tile[0] = lane * 4 + i;
-        s_tile[1] = (ms - start) * kMgBM;
-      }
-      start += tc[i];
+    int te, tm, tn;
+    const bool ok = grouped_gemm_tile(cnt, E, kMgBM, n_tiles, kMgMBlock, lane, te, tm, tn);
+    if (lane == 0) {
+      s_tile[0] = ok ? te : -1;
+      s_tile[1] = tm;
+      s_tile[2] = tn;
     }
   }
   __syncthreads();
   const int e = s_tile[0];
   if (e < 0) return;                                         // block-uniform
   const int m0 = s_tile[1];
+  const int nt = s_tile[2];
   const int M = cnt[e];
   const int row0 = off[e];
   const int n0 = nt * kMgBN;
@@ -362,7 +344,7 @@ hipError_t launch(const void* A, const void* Wq, const void* Ws, const void* bia
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_mxfp4_kernel<GATE_UP>), dim3((unsigned)grid), dim3(kMgThreads), 0, stream,
                      (const bf16_t*)A, (const uint8_t*)Wq, (const uint8_t*)Ws, (const bf16_t*)bias, cnt, off, rows,
-                     K, N, E, k, (int)a_rows, n_tiles, (int)m_slots, out);
+                     K, N, E, k, (int)a_rows, n_tiles, out);
   return hipGetLastError();
 }
 
