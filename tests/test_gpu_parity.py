@@ -121,6 +121,21 @@ def test_route_configs(name, method):
     assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, lg, cfg.k)
 
 
+@pytest.mark.parametrize("seed", [1, 2, 3, 7, 11])
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
+def test_route_configs_other_seeds(name, seed):
+    """The default router (exact at c4, the MFMA router with its exact
+    near-tie recomputation at c3 and c5) on other draws of x, the router and
+    its bias: every token's ids and weights against the oracle."""
+    _need_gpu()
+    cfg = d.CONFIGS[name]
+    x = d.make_activations(cfg, seed=seed)
+    Wr, br = d.make_router(cfg, seed=seed)
+    ids, w = binding.moe_route(dev(x), dev(Wr), dev(br), cfg.k)
+    ids_ref, w_ref, lg = orc.route(x, Wr, br, cfg.k)
+    assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, lg, cfg.k)
+
+
 # ---------------------------------------------------------------------------
 # permutation
 # ---------------------------------------------------------------------------
