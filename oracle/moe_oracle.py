@@ -22,7 +22,7 @@ MoE support" page):
 Everything is computed in float64 from the exactly widened bf16 inputs;
 nothing is rounded except where a reading below says so.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * R1  softmax over the k selected logits (softmax over all E followed by
       renormalising over the top k is the same number);
@@ -221,7 +221,7 @@ def moe_forward_padded(x, Wr, br, Wgu, bgu, Wd, bd, k: int, n_valid: int):
 # --------------------------------------------------------------------------
 # MXFP4 expert weights (section 5 of the Phase 19 page, "MXFP4 W4A16": the
 # weights are 4-bit E2M1 values with one UE8M0 power-of-two scale per 32
-# values; activations stay bf16).  Readings (listed in the design doc):
+# values; activations stay bf16).  Readings where the page is silent:
 #   M1  a block is 32 consecutive values along the contraction dimension K
 #       (the dimension a dot product runs over), so the codes are stored
 #       K-contiguous: codes [E][N][K/2] (byte i of row n holds k = 2i in bits
@@ -311,7 +311,7 @@ def moe_forward_mxfp4(x, Wr, br, Wgu_q, Wgu_s, bgu, Wd_q, Wd_s, bd, k: int, toke
 # --------------------------------------------------------------------------
 # FP8 W8A8 (section 5 of the Phase 19 page: 8-bit weights with one scalar
 # scale per expert, stored transposed [E][N][K]; the scales applied after the
-# product).  Readings (listed in the design doc):
+# product).  Readings where the page is silent:
 #   F1  the 8-bit format is OCP FP8 E4M3 (bias 7, no infinities, largest
 #       finite 448, S.1111.111 is NaN); conversion to it rounds to nearest
 #       with ties to the even code and saturates to +-448; NaN becomes 0x7F;
