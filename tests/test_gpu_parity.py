@@ -465,13 +465,15 @@ def test_padded_graph_replay():
 _weights_cache = {}
 
 
-def _config_inputs(name):
+def _config_inputs(name, seed=0):
+    """The workload's tensors; seed draws x and the router (the expert weights
+    are always seed 0's, which keeps one set per E in memory)."""
     cfg = d.CONFIGS[name]
     if cfg.E not in _weights_cache:
         _weights_cache.clear()
         _weights_cache[cfg.E] = d.make_experts(cfg)
-    x = d.make_activations(cfg)
-    Wr, br = d.make_router(cfg)
+    x = d.make_activations(cfg, seed=seed)
+    Wr, br = d.make_router(cfg, seed=seed)
     Wgu, bgu, Wd, bd = _weights_cache[cfg.E]
     return cfg, (x, Wr, br, Wgu, bgu, Wd, bd)
 
@@ -494,5 +496,26 @@ def test_forward_configs(name):
     ref = orc.moe_forward(*arrays, k=k)
     assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], ref["logits"], k)
     assert_y_close(host_f64(y), ref["y"], f"y {name}")
+    del args
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["c5", "c3"])
+def test_forward_configs_other_seed(name):
+    """The prefill workloads with x and the router drawn at another seed:
+    other per-expert counts, so other tail tiles and another tile order in
+    the grouped-GEMM launches; every token's y against the oracle."""
+    _need_gpu()
+    cfg, arrays = _config_inputs(name, seed=1)
+    k = cfg.k
+    args = [dev(a) for a in arrays]
+    ids = torch.empty((cfg.T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, k), dtype=torch.float32, device="cuda")
+    y = binding.moe_forward(*args, k=k, topk_ids=ids, topk_w=w)
+    torch.cuda.synchronize()
+    print(f"[parity] bf16 {name} seed 1: GPU forward done, running the oracle over all {cfg.T} tokens", flush=True)
+    ref = orc.moe_forward(*arrays, k=k)
+    assert_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], ref["logits"], k)
+    assert_y_close(host_f64(y), ref["y"], f"y {name} seed 1")
     del args
     torch.cuda.empty_cache()
